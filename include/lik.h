@@ -1,0 +1,199 @@
+/*
+ * lik.h -- C ABI of the MI355X (gfx950) fused MaxSim late-interaction scorer.
+ *
+ * What is computed (README "Late Interaction Kernels", section "What does it
+ * compute?"):
+ *
+ *     score(q, d) = sum over valid query tokens i of
+ *                   max over valid document tokens j of  Q[q,i,:] . D[d,j,:]
+ *
+ * with the rules of the README's "Scoring interface" section:
+ *   - masks are bytes, nonzero = valid token; a NULL mask means every token
+ *     is valid;
+ *   - a query mask removes tokens from the sum, a document mask removes
+ *     tokens from the max (a masked token never wins, whatever its value);
+ *   - a document with no valid token scores exactly -1e9 for every query;
+ *   - raw dot products, no normalisation inside; scores are float32.
+ * The "Precision and compatibility" section fixes the input types: float16,
+ * bfloat16 and float32, with float32 accumulation.
+ *
+ * The [Nq, Nd, Lq, Ld] similarity grid is never written to device memory
+ * (social thread, post (4/N): stream document tiles through on-chip memory,
+ * keep a running max in registers).  The backward is fused as well (post
+ * (5/N)) and produces only the input gradients (colpali pull request,
+ * section "Results").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer is a DEVICE pointer on the current HIP device.
+ *   Tensors are dense, row-major, embedding dim innermost.  The caller owns
+ *   all memory; the library never allocates or frees device memory, never
+ *   synchronises, and keeps no pointer after returning.  Q, D, the outputs
+ *   and the workspace must be 16-byte aligned.
+ * Stream.  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   All work is enqueued on it; results are valid once it has drained.
+ * Workspace.  Scratch memory comes only from `workspace`, whose size must be
+ *   at least lik_workspace_bytes(...) for the same operation and shapes.
+ * Outputs.  Every output element is written, so outputs need no clearing.
+ *   Gradients are float32 and OVERWRITTEN (not accumulated).
+ * Argmax.  int32, the document-token index j that reached the max for each
+ *   (pair, query token), ties to the lowest j; -1 for masked query tokens
+ *   and for documents with no valid token.
+ * Errors.  Arguments are checked on the host before any device work; on an
+ *   error nothing is enqueued, no output is touched and a status is
+ *   returned (lik_last_error() gives the detail, per host thread).
+ *   LIK_ERR_INVALID_ARG   null required pointer, negative or overflowing
+ *                         size, unknown dtype, misaligned pointer, workspace
+ *                         too small;
+ *   LIK_ERR_UNSUPPORTED   a valid request this build does not implement
+ *                         (see lik_supported_dim; backward with Ld >
+ *                         16000; no gfx950 device);
+ *   LIK_ERR_HIP           a HIP launch error, reported as it happens.
+ *   Zero-sized batches (Nq, Nd, B or N of 0) are a successful no-op.
+ * Determinism.  For identical inputs and shapes the results are bitwise
+ *   identical run to run: no floating-point atomics are used anywhere.
+ * Reentrancy.  Calls may be made from several host threads; calls that share
+ *   a workspace on overlapping streams race on it.
+ */
+#ifndef LIK_H_
+#define LIK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIK_ABI_VERSION 1
+
+typedef enum { LIK_F16 = 0, LIK_BF16 = 1, LIK_F32 = 2 } lik_dtype;
+
+typedef enum {
+  LIK_OK = 0,
+  LIK_ERR_INVALID_ARG = 1,
+  LIK_ERR_UNSUPPORTED = 2,
+  LIK_ERR_HIP = 3
+} lik_status;
+
+/* Operation codes for lik_workspace_bytes. */
+typedef enum {
+  LIK_OP_FWD = 0,          /* all-pairs forward  */
+  LIK_OP_BWD = 1,          /* all-pairs backward */
+  LIK_OP_PAIRWISE_FWD = 2,
+  LIK_OP_PAIRWISE_BWD = 3,
+  LIK_OP_KD_FWD = 4,
+  LIK_OP_KD_BWD = 5
+} lik_op;
+
+/* LIK_ABI_VERSION of the loaded library. */
+int lik_abi_version(void);
+
+/* Static description of a status code. */
+const char* lik_status_string(lik_status s);
+
+/* Detail of the last non-OK status returned on this host thread ("" if none). */
+const char* lik_last_error(void);
+
+/* 1 if the embedding dim `dim` has kernels in this build, else 0. */
+int lik_supported_dim(int64_t dim);
+
+/*
+ * Workspace bytes needed by one call.  Arguments mirror the entry point:
+ *   all-pairs : nq_or_b = Nq, nd_or_n = Nd;
+ *   pairwise  : nq_or_b = B,  nd_or_n = 1 (ignored);
+ *   kd        : nq_or_b = B,  nd_or_n = N.
+ * flags bit 0: forward -- the caller passes an argmax buffer;
+ *              backward -- the caller passes the forward's argmax (if 0, the
+ *              backward recomputes it into the workspace).
+ * flags bit 1: a document mask will be passed.
+ * Returns 0 for zero-sized problems; never fails (returns SIZE_MAX for sizes
+ * that overflow).
+ */
+size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq,
+                           int64_t nd_or_n, int64_t ld, int64_t dim,
+                           lik_dtype dtype, int flags);
+
+/*
+ * All-pairs forward (README "Scoring interface", layer MaxSim):
+ *   Q [Nq, Lq, dim] x D [Nd, Ld, dim] -> scores [Nq, Nd] float32.
+ * q_mask [Nq, Lq] bytes or NULL; d_mask [Nd, Ld] bytes or NULL.
+ * argmax [Nq, Nd, Lq] int32, or NULL to not keep it.
+ */
+lik_status lik_maxsim_fwd(const void* Q, const void* D, lik_dtype dtype,
+                          int64_t Nq, int64_t Lq, int64_t Nd, int64_t Ld,
+                          int64_t dim, const uint8_t* q_mask,
+                          const uint8_t* d_mask, float* scores,
+                          int32_t* argmax, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * All-pairs backward: gradients of sum(grad_scores * scores).
+ *   grad_Q[q,i,:] = sum over non-empty d of grad_scores[q,d] * D[d, a(q,d,i), :]
+ *   grad_D[d,j,:] = sum over (q, valid i) with a(q,d,i) = j of
+ *                   grad_scores[q,d] * Q[q,i,:]
+ * (all other rows exactly 0).  grad_scores [Nq, Nd] float32.  argmax is the
+ * forward's output for the same inputs, or NULL to recompute it.  grad_Q
+ * [Nq, Lq, dim] and grad_D [Nd, Ld, dim] are float32; either may be NULL to
+ * skip it.  grad_D's rows are each summed by one owner in a fixed order.
+ */
+lik_status lik_maxsim_bwd(const void* Q, const void* D, lik_dtype dtype,
+                          int64_t Nq, int64_t Lq, int64_t Nd, int64_t Ld,
+                          int64_t dim, const uint8_t* q_mask,
+                          const uint8_t* d_mask, const float* grad_scores,
+                          const int32_t* argmax, float* grad_Q, float* grad_D,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * Pairwise forward (README "Scoring interface", layer MaxSimPairwise):
+ *   Q [B, Lq, dim] x D [B, Ld, dim] -> scores [B]; query b meets document b
+ *   only.  q_mask [B, Lq], d_mask [B, Ld] or NULL; argmax [B, Lq] or NULL.
+ */
+lik_status lik_maxsim_pairwise_fwd(const void* Q, const void* D,
+                                   lik_dtype dtype, int64_t B, int64_t Lq,
+                                   int64_t Ld, int64_t dim,
+                                   const uint8_t* q_mask,
+                                   const uint8_t* d_mask, float* scores,
+                                   int32_t* argmax, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Pairwise backward: grad_scores [B]; grad_Q [B, Lq, dim]; grad_D [B, Ld, dim]. */
+lik_status lik_maxsim_pairwise_bwd(const void* Q, const void* D,
+                                   lik_dtype dtype, int64_t B, int64_t Lq,
+                                   int64_t Ld, int64_t dim,
+                                   const uint8_t* q_mask,
+                                   const uint8_t* d_mask,
+                                   const float* grad_scores,
+                                   const int32_t* argmax, float* grad_Q,
+                                   float* grad_D, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * kd (per-query candidate) forward (colpali pull request, section "Design":
+ * the [B, N, Ld, d] candidate layout of the negative-document losses):
+ *   Q [B, Lq, dim] x D [B, N, Ld, dim] -> scores [B, N]; query b meets its
+ *   own N candidates.  q_mask [B, Lq], d_mask [B, N, Ld] or NULL;
+ *   argmax [B, N, Lq] or NULL.
+ */
+lik_status lik_maxsim_kd_fwd(const void* Q, const void* D, lik_dtype dtype,
+                             int64_t B, int64_t Lq, int64_t N, int64_t Ld,
+                             int64_t dim, const uint8_t* q_mask,
+                             const uint8_t* d_mask, float* scores,
+                             int32_t* argmax, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* kd backward: grad_scores [B, N]; grad_Q [B, Lq, dim]; grad_D [B, N, Ld, dim]. */
+lik_status lik_maxsim_kd_bwd(const void* Q, const void* D, lik_dtype dtype,
+                             int64_t B, int64_t Lq, int64_t N, int64_t Ld,
+                             int64_t dim, const uint8_t* q_mask,
+                             const uint8_t* d_mask, const float* grad_scores,
+                             const int32_t* argmax, float* grad_Q,
+                             float* grad_D, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIK_H_ */

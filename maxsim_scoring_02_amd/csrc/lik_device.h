@@ -1,0 +1,229 @@
+// Device-side building blocks of the gfx950 MaxSim kernels.
+//
+// MaxSim (README "Late Interaction Kernels", "What does it compute?"):
+//   score(q,d) = sum_{valid i} max_{valid j} Q[q,i,:] . D[d,j,:]
+//
+// Orientation.  One 32x32 MFMA output tile is S^T = Dtile (32 doc rows) x
+// Q^T (32 query-token columns).  In the 32x32 accumulator layout lane l owns
+// column l%32 and 16 rows {8*(v/4) + 4*(l/32) + v%4 : v = 0..15}, so the max
+// over document tokens is mostly a per-lane reduction; lanes l and l^32 hold
+// the two row halves of the same column and meet once per (column, unit).
+//
+// K mapping.  Each lane feeds the MFMA 16-byte chunks of its row: lane
+// (row or column r, half h = l/32) supplies chunk 2m+h at K-step m.  A and B
+// use the same mapping, so every product Q[.,k]*D[.,k] is summed exactly once
+// (the order of the K-sum is the only freedom taken).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lik {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kTile = 32;   // document rows per tile (MFMA M)
+constexpr int kWave = 64;
+
+enum class Elem { F16 = 0, BF16 = 1, F32 = 2 };
+
+template <Elem E> struct ElemInfo;
+template <> struct ElemInfo<Elem::F16>  { static constexpr int kBytes = 2; static constexpr int kPerChunk = 8; };
+template <> struct ElemInfo<Elem::BF16> { static constexpr int kBytes = 2; static constexpr int kPerChunk = 8; };
+template <> struct ElemInfo<Elem::F32>  { static constexpr int kBytes = 4; static constexpr int kPerChunk = 4; };
+
+// Geometry of one document row / tile for an element type and embedding dim.
+template <Elem E, int DIM>
+struct Geo {
+  static constexpr int kRowBytes = DIM * ElemInfo<E>::kBytes;
+  static constexpr int kCPR = kRowBytes / 16;            // 16-byte chunks per row
+  static constexpr int kKSteps = kCPR / 2;               // chunks each lane feeds
+  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kTileChunks = kTile * kCPR;
+  static constexpr int kSwz = kCPR < 16 ? kCPR : 16;     // XOR swizzle span
+  static_assert(kCPR % 2 == 0 && kCPR >= 2, "dim must give an even chunk count");
+};
+
+// Physical LDS byte offset of (row r, chunk c) in a swizzled tile: the chunk
+// index is XORed with the row so that the 32 rows read by one MFMA operand
+// load fall in distinct banks.
+template <Elem E, int DIM>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  using G = Geo<E, DIM>;
+  return r * G::kRowBytes + ((c ^ (r & (G::kSwz - 1))) << 4);
+}
+
+__device__ __forceinline__ u32x4 ld_global_16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld_lds_16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void st_lds_16(char* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+// acc += A(32 x k) * B(k x 32) for one 16-byte chunk per lane.
+template <Elem E> __device__ __forceinline__ void mfma_chunk(f32x16& acc, u32x4 a, u32x4 b);
+
+template <> __device__ __forceinline__ void mfma_chunk<Elem::BF16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma_chunk<Elem::F16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                               __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+// Vector elements are read into scalars before reinterpretation: a bit-cast
+// applied directly to an element lvalue of an ext_vector reads element 0.
+template <> __device__ __forceinline__ void mfma_chunk<Elem::F32>(f32x16& acc, u32x4 a, u32x4 b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ae = a[e], be = b[e];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ae), __uint_as_float(be), acc, 0,
+                                               0, 0);
+  }
+}
+
+// Row of accumulator element v for a lane in half h (32x32 MFMA layout).
+__device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+// Validity word of tile t (bit r = doc row 32t+r is a valid token).
+__device__ __forceinline__ uint32_t tile_word(const uint32_t* bits_d, int t, int64_t Ld) {
+  if (bits_d) return bits_d[t];
+  int64_t rem = Ld - (int64_t)t * kTile;
+  return rem >= kTile ? 0xffffffffu : ((1u << rem) - 1u);
+}
+
+// Running state of one 32-column block: the best value seen by this lane,
+// the tile it came from and that tile's 16 values (to recover the row).
+struct BlockState {
+  float run_max;
+  int best_tile;
+  float best_val[16];
+};
+
+__device__ __forceinline__ void state_init(BlockState& s, int t0) {
+  s.run_max = -__builtin_inff();
+  s.best_tile = t0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s.best_val[v] = -__builtin_inff();
+}
+
+// Fold one tile's accumulator into the running state.  `word` masks rows
+// (masked rows never win).  Strict '>' keeps the earlier tile on ties.
+__device__ __forceinline__ void state_update(BlockState& s, f32x16 acc, uint32_t word, int t, int h) {
+  if (word != 0xffffffffu) {
+    uint32_t w = word >> (4 * h);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int bit = 8 * (v >> 2) + (v & 3);
+      if (!((w >> bit) & 1u)) acc[v] = -__builtin_inff();
+    }
+  }
+  float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
+  float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
+  float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
+  float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
+  float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
+  float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
+  float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
+  float tmax = __builtin_fmaxf(m1, m2);
+  bool better = tmax > s.run_max;
+  s.run_max = better ? tmax : s.run_max;
+  s.best_tile = better ? t : s.best_tile;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s.best_val[v] = better ? acc[v] : s.best_val[v];
+}
+
+// (max, lowest doc row reaching it) of this lane's half-column.
+__device__ __forceinline__ void state_resolve(const BlockState& s, int h, float& M, int& J) {
+  int kk = 15;
+#pragma unroll
+  for (int v = 14; v >= 0; --v) kk = (s.best_val[v] == s.run_max) ? v : kk;
+  M = s.run_max;
+  J = s.best_tile * kTile + acc_row(kk, h);
+}
+
+// Larger value wins; equal values keep the lower index.
+__device__ __forceinline__ void merge_mj(float& M, int& J, float M2, int J2) {
+  bool take = (M2 > M) || (M2 == M && J2 < J);
+  M = take ? M2 : M;
+  J = take ? J2 : J;
+}
+
+// After the two row halves of a column are merged, lane L of the wave holds
+// the result of slot L (NB == 2: block L/32, column L%32) or slot L%32
+// (NB == 1, both halves hold it).
+template <int NB>
+__device__ __forceinline__ void combine_halves(const float (&M)[NB], const int (&J)[NB], int lane,
+                                               float& Mout, int& Jout) {
+  if constexpr (NB == 2) {
+    bool lo = lane < 32;
+    float own_m = lo ? M[0] : M[1];
+    int own_j = lo ? J[0] : J[1];
+    float give_m = lo ? M[1] : M[0];
+    int give_j = lo ? J[1] : J[0];
+    float oth_m = __shfl_xor(give_m, 32);
+    int oth_j = __shfl_xor(give_j, 32);
+    merge_mj(own_m, own_j, oth_m, oth_j);
+    Mout = own_m;
+    Jout = own_j;
+  } else {
+    float own_m = M[0];
+    int own_j = J[0];
+    merge_mj(own_m, own_j, __shfl_xor(own_m, 32), __shfl_xor(own_j, 32));
+    Mout = own_m;
+    Jout = own_j;
+  }
+}
+
+// Inclusive sum of v over the lanes of a segment [seg_start, lane] (segments
+// are contiguous lane ranges inside groups of `width` lanes).
+template <int WIDTH>
+__device__ __forceinline__ float segmented_scan(float v, int lane_in, int seg_start) {
+#pragma unroll
+  for (int k = 1; k < WIDTH; k <<= 1) {
+    float t = __shfl_up(v, k, WIDTH);
+    if (lane_in - k >= seg_start) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+  return v;
+}
+
+// Element conversion for the backward's float32 arithmetic.
+template <Elem E> __device__ __forceinline__ void chunk_to_float(u32x4 c, float (&f)[ElemInfo<E>::kPerChunk]);
+template <> __device__ __forceinline__ void chunk_to_float<Elem::BF16>(u32x4 c, float (&f)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = c[k];
+    f[2 * k] = __uint_as_float(w << 16);
+    f[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void chunk_to_float<Elem::F16>(u32x4 c, float (&f)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = c[k];
+    const uint16_t lo = (uint16_t)(w & 0xffffu), hi = (uint16_t)(w >> 16);
+    f[2 * k] = (float)__builtin_bit_cast(_Float16, lo);
+    f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, hi);
+  }
+}
+template <> __device__ __forceinline__ void chunk_to_float<Elem::F32>(u32x4 c, float (&f)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = c[k];
+    f[k] = __uint_as_float(w);
+  }
+}
+
+}  // namespace lik

@@ -1,0 +1,40 @@
+// Internal interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lik_plan.h"
+
+namespace lik {
+
+// Arguments of the forward kernels (passed by value).
+struct FwdArgs {
+  const void* Q;
+  const void* D;
+  const uint8_t* q_mask;
+  uint32_t* bits;     // [n_docs][nwords] tile validity words, or null (no doc mask)
+  int32_t* ntiles;    // [n_docs] tiles up to the last valid token, or null
+  float* scores;
+  int32_t* argmax;
+  float* part_M;            // partial maxima  [nchunks][n_docs][n_cg][SPW]
+  int32_t* part_J;          // partial argmaxes, same layout
+  int layout;
+  int SPW;
+  int partial;
+  int64_t Nq, Lq, n_docs, Ld, K;
+  int64_t nwords, ntiles_max;
+  int64_t qpw, n_cg, n_sb, nchunks, tpc, upw, n_groups, gpx, n_units;
+};
+
+bool fwd_dim_supported(int64_t dim);
+
+hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uint8_t* q_mask,
+                       const uint8_t* d_mask, float* scores, int32_t* argmax, char* ws,
+                       hipStream_t s);
+
+hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const uint8_t* q_mask,
+                        const uint8_t* d_mask, const float* grad_scores, const int32_t* argmax,
+                        float* grad_Q, float* grad_D, char* ws, hipStream_t s);
+
+}  // namespace lik

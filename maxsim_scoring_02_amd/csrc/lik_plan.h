@@ -1,0 +1,182 @@
+// Launch plans shared by the C ABI (host) and the kernels: how a MaxSim call
+// is cut into work units and where its scratch lives in the workspace.
+// Plans depend on shapes only, never on data, so the workspace size can be
+// queried before any device memory exists.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lik {
+
+enum Layout : int { kAllPairs = 0, kPairwise = 1, kKd = 2 };
+
+struct FwdPlan {
+  int layout = 0;
+  int elem = 0;             // 0 f16, 1 bf16, 2 f32
+  int dim = 0;
+  int NB = 2;               // 32-column MFMA blocks per wave
+  int SPW = 64;             // query-token slots per wave (32 * NB)
+  int64_t Nq = 0, Lq = 0;   // queries (B for pairwise/kd) and tokens per query
+  int64_t n_docs = 0;       // documents (Nd; B; B*N)
+  int64_t Ld = 0;
+  int64_t K = 1;            // documents per query for pairwise (1) / kd (N)
+  int64_t nwords = 0;       // 32-bit mask words per document
+  int64_t ntiles_max = 0;   // ceil(Ld / 32)
+  bool has_dmask = false;
+  bool partial = false;     // per-slot partials + combine kernel
+  // slot mapping (all-pairs): qpw > 0 packs qpw whole queries per wave,
+  // qpw == 0 flattens (q, i) so a query may span waves.
+  int64_t qpw = 0;
+  int64_t n_cg = 0;         // column groups: waves (all-pairs) or slot groups per query (pairs)
+  int NW = 8;               // waves per workgroup (all-pairs)
+  int64_t n_sb = 0;         // slot blocks (all-pairs)
+  int64_t nchunks = 1, tpc = 0;  // split of a document's tiles
+  int64_t upw = 1;          // units per workgroup (all-pairs)
+  int64_t n_groups = 0, gpx = 0;
+  int64_t n_units = 0;      // pairs: waves launched
+  // workspace layout (bytes)
+  size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, fwd_bytes = 0;
+};
+
+struct BwdPlan {
+  FwdPlan fwd;              // used when the argmax must be recomputed
+  bool recompute = false;
+  int64_t H = 0;            // hits per document (all-pairs Nq*Lq; pairs Lq)
+  int key_bits = 1;
+  size_t off_argmax = 0, off_scores = 0, off_sorted = 0, off_roff = 0, off_fwd = 0, total = 0;
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Number of 32-column blocks per wave for an element type and dim.
+inline int blocks_per_wave(int elem, int64_t dim) {
+  if (elem == 2) return 1;
+  return dim <= 128 ? 2 : 1;
+}
+
+inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
+                             int64_t nd_or_n, int64_t Ld, int64_t dim, bool has_dmask,
+                             bool keep_argmax) {
+  (void)keep_argmax;
+  FwdPlan p;
+  p.layout = layout;
+  p.elem = elem;
+  p.dim = (int)dim;
+  p.NB = blocks_per_wave(elem, dim);
+  p.SPW = 32 * p.NB;
+  p.Nq = nq_or_b;
+  p.Lq = Lq;
+  p.Ld = Ld;
+  p.has_dmask = has_dmask;
+  if (layout == kAllPairs) {
+    p.n_docs = nd_or_n;
+    p.K = 0;
+  } else if (layout == kPairwise) {
+    p.n_docs = nq_or_b;
+    p.K = 1;
+  } else {
+    p.n_docs = nq_or_b * nd_or_n;
+    p.K = nd_or_n;
+  }
+  p.nwords = cdiv(Ld, 32);
+  p.ntiles_max = p.nwords;
+  if (p.Nq == 0 || p.n_docs == 0) return p;  // nothing to do
+
+  size_t off = 0;
+  if (has_dmask) {
+    p.off_bits = off;
+    off = align256(off + (size_t)p.n_docs * p.nwords * 4);
+    p.off_tiles = off;
+    off = align256(off + (size_t)p.n_docs * 4);
+  }
+  if (Lq == 0) {  // only the empty-document test is needed
+    p.fwd_bytes = off;
+    return p;
+  }
+
+  if (layout == kAllPairs) {
+    if (Lq <= p.SPW) {
+      p.qpw = p.SPW / Lq;
+      p.n_cg = cdiv(p.Nq, p.qpw);
+    } else {
+      p.qpw = 0;
+      p.n_cg = cdiv(p.Nq * Lq, p.SPW);
+    }
+    p.NW = 8;
+    p.n_sb = cdiv(p.n_cg, p.NW);
+    // Long documents are cut into chunks of 32 tiles (1024 rows) so that
+    // work units stay short and the chip fills; chunk maxima merge exactly.
+    if (p.ntiles_max > 64) {
+      p.tpc = 32;
+      p.nchunks = cdiv(p.ntiles_max, p.tpc);
+    } else {
+      p.tpc = p.ntiles_max > 0 ? p.ntiles_max : 1;
+      p.nchunks = 1;
+    }
+    p.partial = (p.nchunks > 1) || (p.qpw == 0);
+    int64_t units = p.n_docs * p.nchunks;
+    // About 1024 workgroups; each keeps its query fragments for upw units.
+    int64_t target = 1024;
+    int64_t per_sb = cdiv(target, p.n_sb);
+    p.upw = per_sb >= units ? 1 : cdiv(units, per_sb);
+    if (p.upw < 1) p.upw = 1;
+    p.n_groups = cdiv(units, p.upw);
+    p.gpx = cdiv(p.n_groups, 8);
+  } else {
+    p.n_cg = cdiv(Lq, p.SPW);
+    int64_t pairs = p.n_docs * p.n_cg;
+    int64_t want = 4096;
+    int64_t nch = pairs >= want ? 1 : cdiv(want, pairs);
+    int64_t max_nch = p.ntiles_max >= 4 ? p.ntiles_max / 4 : 1;
+    if (nch > max_nch) nch = max_nch;
+    if (nch < 1) nch = 1;
+    p.tpc = p.ntiles_max > 0 ? cdiv(p.ntiles_max, nch) : 1;
+    p.nchunks = p.ntiles_max > 0 ? cdiv(p.ntiles_max, p.tpc) : 1;
+    p.partial = (p.nchunks > 1) || (p.n_cg > 1);
+    p.n_units = pairs * p.nchunks;
+  }
+  if (p.partial) {
+    size_t n = (size_t)p.nchunks * p.n_docs * p.n_cg * p.SPW;
+    p.off_partM = off;
+    off = align256(off + n * 4);
+    p.off_partJ = off;
+    off = align256(off + n * 4);
+  }
+  p.fwd_bytes = off;
+  return p;
+}
+
+inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, int64_t nd_or_n,
+                             int64_t Ld, int64_t dim, bool has_dmask, bool have_argmax) {
+  BwdPlan b;
+  b.fwd = make_fwd_plan(layout, elem, nq_or_b, Lq, nd_or_n, Ld, dim, has_dmask, true);
+  const FwdPlan& f = b.fwd;
+  if (f.Nq == 0 || f.n_docs == 0) return b;
+  b.recompute = !have_argmax;
+  b.H = (layout == kAllPairs) ? f.Nq * Lq : Lq;
+  int bits = 1;
+  while (bits < 31 && (int64_t(1) << bits) < Ld) ++bits;
+  b.key_bits = bits;
+  size_t off = 0;
+  if (b.recompute && Lq > 0) {
+    int64_t pairs = (layout == kAllPairs) ? f.Nq * f.n_docs : f.n_docs;
+    b.off_argmax = off;
+    off = align256(off + (size_t)pairs * Lq * 4);
+    b.off_scores = off;
+    off = align256(off + (size_t)pairs * 4);
+    b.off_fwd = off;
+    off = align256(off + f.fwd_bytes);
+  }
+  if (Lq > 0 && Ld > 0) {
+    b.off_sorted = off;
+    off = align256(off + (size_t)f.n_docs * b.H * 4);
+    b.off_roff = off;
+    off = align256(off + (size_t)f.n_docs * (Ld + 1) * 4);
+  }
+  b.total = off;
+  return b;
+}
+
+}  // namespace lik

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/lik.h declares, and rejects bad calls with the documented status
+before any device work.  No GPU is needed: every call below fails argument
+validation (or is a zero-sized no-op), so nothing is launched and the fake
+pointers are never dereferenced."""
+
+import ctypes
+
+import pytest
+
+from maxsim_scoring_02_amd import _lib
+from maxsim_scoring_02_amd._lib import (LIK_BF16, LIK_ERR_INVALID_ARG, LIK_ERR_UNSUPPORTED,
+                                        LIK_F16, LIK_F32, LIK_OK, LIK_OP_BWD, LIK_OP_FWD,
+                                        LIK_OP_KD_BWD, LIK_OP_KD_FWD, LIK_OP_PAIRWISE_BWD,
+                                        LIK_OP_PAIRWISE_FWD)
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # 16-byte aligned, never dereferenced
+MIS = P(0x1004)           # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = _lib.header_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(L, n), f"liblik.so does not export {n}"
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_version_and_status_strings(L):
+    assert L.lik_abi_version() == 1
+    assert L.lik_status_string(LIK_OK) == b"ok"
+    assert L.lik_status_string(LIK_ERR_INVALID_ARG) == b"invalid argument"
+    assert L.lik_status_string(LIK_ERR_UNSUPPORTED) == b"unsupported"
+    assert L.lik_supported_dim(128) == 1 and L.lik_supported_dim(64) == 1
+    assert L.lik_supported_dim(100) == 0 and L.lik_supported_dim(0) == 0
+
+
+def fwd(L, **kw):
+    a = dict(Q=FAKE, D=FAKE, dtype=LIK_BF16, Nq=2, Lq=32, Nd=3, Ld=40, dim=128, qm=None,
+             dm=None, scores=FAKE, argmax=None, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return L.lik_maxsim_fwd(a["Q"], a["D"], a["dtype"], a["Nq"], a["Lq"], a["Nd"], a["Ld"],
+                            a["dim"], a["qm"], a["dm"], a["scores"], a["argmax"], a["ws"],
+                            a["wsb"], a["stream"])
+
+
+def bwd(L, **kw):
+    a = dict(Q=FAKE, D=FAKE, dtype=LIK_BF16, Nq=2, Lq=32, Nd=3, Ld=40, dim=128, qm=None,
+             dm=None, g=FAKE, argmax=FAKE, gQ=FAKE, gD=FAKE, ws=FAKE, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return L.lik_maxsim_bwd(a["Q"], a["D"], a["dtype"], a["Nq"], a["Lq"], a["Nd"], a["Ld"],
+                            a["dim"], a["qm"], a["dm"], a["g"], a["argmax"], a["gQ"], a["gD"],
+                            a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(Q=None), "Q is NULL"),
+    (dict(D=None), "D is NULL"),
+    (dict(scores=None), "scores is NULL"),
+    (dict(Nq=-1), "negative"),
+    (dict(Ld=-5), "negative"),
+    (dict(dtype=7), "dtype"),
+    (dict(Q=MIS), "aligned"),
+    (dict(argmax=MIS), "aligned"),
+    (dict(Nq=1 << 40, Nd=1 << 40), "overflow"),
+])
+def test_forward_rejects_invalid_arguments(L, kw, msg):
+    assert fwd(L, **kw) == LIK_ERR_INVALID_ARG
+    assert msg in L.lik_last_error().decode()
+
+
+def test_forward_rejects_small_workspace(L):
+    need = L.lik_workspace_bytes(LIK_OP_FWD, 2, 32, 3, 40, 128, LIK_BF16, 2)
+    assert need > 0
+    assert fwd(L, dm=FAKE, wsb=need - 1) == LIK_ERR_INVALID_ARG
+    assert "workspace too small" in L.lik_last_error().decode()
+    assert fwd(L, dm=FAKE, ws=None, wsb=need) == LIK_ERR_INVALID_ARG
+
+
+def test_unsupported_dim_is_reported_before_device_work(L):
+    assert fwd(L, dim=100) == LIK_ERR_UNSUPPORTED
+    assert "dim" in L.lik_last_error().decode()
+    assert bwd(L, dim=48) == LIK_ERR_UNSUPPORTED
+
+
+def test_backward_rejects_invalid_arguments(L):
+    assert bwd(L, g=None) == LIK_ERR_INVALID_ARG
+    assert bwd(L, gD=MIS) == LIK_ERR_INVALID_ARG
+    assert bwd(L, wsb=0) == LIK_ERR_INVALID_ARG
+    assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
+
+
+def test_zero_sized_calls_are_ok_noops(L):
+    assert fwd(L, Nq=0, Q=None, scores=None) == LIK_OK
+    assert fwd(L, Nd=0, D=None, scores=None) == LIK_OK
+    assert bwd(L, Nq=0, Q=None, g=None) == LIK_OK
+    assert bwd(L, gQ=None, gD=None) == LIK_OK          # nothing requested
+    assert L.lik_maxsim_kd_fwd(FAKE, FAKE, LIK_F16, 4, 32, 0, 40, 128, None, None, None, None,
+                               None, 0, None) == LIK_OK
+    assert L.lik_maxsim_pairwise_fwd(None, None, LIK_F32, 0, 32, 40, 128, None, None, None,
+                                     None, None, 0, None) == LIK_OK
+
+
+def test_workspace_bytes_monotone_and_layouts(L):
+    w = lambda *a: L.lik_workspace_bytes(*a)
+    assert w(LIK_OP_FWD, 0, 32, 5, 40, 128, LIK_BF16, 3) == 0
+    # a document mask needs tile words; no mask and short docs need nothing
+    assert w(LIK_OP_FWD, 256, 32, 256, 300, 128, LIK_BF16, 1) == 0
+    assert w(LIK_OP_FWD, 256, 32, 256, 300, 128, LIK_BF16, 3) > 0
+    # split long documents need partial maxima
+    assert w(LIK_OP_PAIRWISE_FWD, 64, 32, 1, 32768, 128, LIK_F16, 0) > 0
+    # the backward without argmax holds a recomputed one
+    with_am = w(LIK_OP_BWD, 256, 32, 256, 300, 128, LIK_BF16, 1)
+    without = w(LIK_OP_BWD, 256, 32, 256, 300, 128, LIK_BF16, 0)
+    assert without >= with_am + 256 * 256 * 32 * 4
+    for op in (LIK_OP_PAIRWISE_BWD, LIK_OP_KD_BWD, LIK_OP_KD_FWD):
+        assert w(op, 8, 32, 4, 1030, 128, LIK_BF16, 1) < 1 << 30
+    assert w(LIK_OP_FWD, -1, 32, 5, 40, 128, LIK_BF16, 0) == ctypes.c_size_t(-1).value
+    # op memory is linear in the batch for pairs (no B^2 term) and the
+    # all-pairs workspace holds no [Nq, Nd, Lq, Ld] buffer
+    a = w(LIK_OP_KD_BWD, 64, 32, 16, 1030, 128, LIK_BF16, 1)
+    b = w(LIK_OP_KD_BWD, 128, 32, 16, 1030, 128, LIK_BF16, 1)
+    assert b <= 2 * a + 4096
+    big = w(LIK_OP_BWD, 128, 32, 128, 1030, 128, LIK_BF16, 1)
+    assert big < 128 * 128 * 32 * 1030 * 4 / 50
+
+
+def test_device_check_without_a_gpu(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device path is only reachable without one")
+    # a fully valid call reaches the device check and reports no device
+    need = L.lik_workspace_bytes(LIK_OP_FWD, 2, 32, 3, 40, 128, LIK_BF16, 0)
+    assert fwd(L, wsb=need) == LIK_ERR_UNSUPPORTED
+    assert "device" in L.lik_last_error().decode()
