@@ -1,0 +1,447 @@
+"""Benchmark of the fused MaxSim operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+that is already resident in HBM: the forward (scores + int32 argmax) and, for
+training workloads, the backward (grad_Q and grad_D in float32).  W untimed
+steps, then exactly K timed steps between two device synchronisations; rank 0
+prints one JSON line.
+
+Default workload: ColBERT-text in-batch contrastive fwd+bwd -- 256 queries x
+32 tokens against 256 documents padded to 300 tokens (true lengths uniform in
+[64, 300], masked, zero padding), dim 128, bf16, Gaussian upstream grad.
+
+Throughput counts algorithmic work on valid tokens only:
+  forward   2 * dim * sum over (q, d) of Lq_valid(q) * Ld_valid(d)
+  backward  4 * dim * (valid (q, i, d) triples with d non-empty)
+(one gathered row-FMA for grad_Q and one scattered row-FMA for grad_D).
+
+Other workloads (--workload): inbatch-pages, kd-candidates, long-docs,
+long-rerank, or `all` (one line each).  Memory-bound workloads report GB/s of
+compulsory traffic (inputs' valid rows read once, outputs and float32
+gradients written once).
+
+`cpu_baseline` is the CPU oracle timed on this machine's cores on a bounded
+sample of the same workload (the sample is named in the JSON).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MaxSim fwd+bwd TFLOP/s (% MFMA peak); pairwise rerank GB/s (% HBM peak)"
+PEAK_MFMA_16BIT = 2500.0        # TFLOP/s, MI355X dense bf16/fp16
+PEAK_HBM = 8000.0               # GB/s, MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+# --------------------------------------------------------------------------
+# algorithmic work
+# --------------------------------------------------------------------------
+
+def _valid_lengths(w):
+    qv = (np.full(w.Q.shape[0], w.Q.shape[1]) if w.q_mask is None
+          else w.q_mask.numpy().sum(axis=1))
+    dshape = tuple(w.D.shape[:-1])
+    dv = (np.full(dshape[:-1], dshape[-1]) if w.d_mask is None
+          else w.d_mask.numpy().sum(axis=-1))
+    return qv.astype(np.int64), dv.astype(np.int64)
+
+
+def work(w):
+    """(forward flops, backward flops, forward bytes, backward bytes)."""
+    dim = w.dim
+    eb = w.Q.element_size()
+    qv, dv = _valid_lengths(w)
+    if w.layout == "allpairs":
+        pairs_q = np.repeat(qv, len(dv))
+        pairs_d = np.tile(dv, len(qv))
+    elif w.layout == "pairwise":
+        pairs_q, pairs_d = qv, dv
+    else:
+        B, N = dv.shape
+        pairs_q = np.repeat(qv, N)
+        pairs_d = dv.reshape(-1)
+    f_fwd = float(2 * dim * np.sum(pairs_q * pairs_d))
+    f_bwd = float(4 * dim * np.sum(pairs_q * (pairs_d > 0)))
+    n_scores = pairs_q.size
+    Lq = w.Q.shape[1]
+    q_bytes = float(qv.sum() * dim * eb)
+    d_bytes = float(dv.sum() * dim * eb)
+    mask_bytes = (0 if w.q_mask is None else w.q_mask.numel()) + \
+                 (0 if w.d_mask is None else w.d_mask.numel())
+    b_fwd = q_bytes + d_bytes + mask_bytes + n_scores * 4 + n_scores * Lq * 4
+    d_rows = float(np.prod(w.D.shape[:-1]))
+    b_bwd = (q_bytes + d_bytes + n_scores * 4 + n_scores * Lq * 4
+             + w.Q.shape[0] * Lq * dim * 4 + d_rows * dim * 4)
+    return f_fwd, f_bwd, b_fwd, b_bwd
+
+
+# --------------------------------------------------------------------------
+# GPU operator with preallocated buffers (direct C-ABI calls)
+# --------------------------------------------------------------------------
+
+class Op:
+    def __init__(self, w, backward: bool):
+        import torch
+        from maxsim_scoring_02_amd import _lib
+
+        self.torch = torch
+        self.L = _lib.lib()
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        self.Q = w.Q.to(dev).contiguous()
+        self.D = w.D.to(dev).contiguous()
+        self.qm = None if w.q_mask is None else w.q_mask.to(dev).contiguous().view(torch.uint8)
+        self.dm = None if w.d_mask is None else w.d_mask.to(dev).contiguous().view(torch.uint8)
+        self.dt = _lib.DTYPE_CODE[self.Q.dtype]
+        self.backward = backward
+        Lq, dim = w.Q.shape[1], w.dim
+        shape = w.scores_shape
+        self.scores = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.argmax = torch.empty(tuple(shape) + (Lq,), dtype=torch.int32, device=dev)
+        lay = w.layout
+        if lay == "allpairs":
+            self.dims = (w.Q.shape[0], Lq, w.D.shape[0], w.D.shape[1], dim)
+            ops = (_lib.LIK_OP_FWD, _lib.LIK_OP_BWD)
+        elif lay == "pairwise":
+            self.dims = (w.Q.shape[0], Lq, 1, w.D.shape[1], dim)
+            ops = (_lib.LIK_OP_PAIRWISE_FWD, _lib.LIK_OP_PAIRWISE_BWD)
+        else:
+            self.dims = (w.Q.shape[0], Lq, w.D.shape[1], w.D.shape[2], dim)
+            ops = (_lib.LIK_OP_KD_FWD, _lib.LIK_OP_KD_BWD)
+        flags = 1 | (2 if self.dm is not None else 0)
+        self.wsf_n = self.L.lik_workspace_bytes(ops[0], *self.dims, self.dt, flags)
+        self.wsb_n = self.L.lik_workspace_bytes(ops[1], *self.dims, self.dt, flags)
+        mk = lambda n: torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self.wsf = mk(self.wsf_n)
+        self.wsb = mk(self.wsb_n)
+        if backward:
+            g = w.grad if w.grad is not None else None
+            self.g = (g.to(dev).contiguous() if g is not None
+                      else torch.zeros(shape, dtype=torch.float32, device=dev))
+            self.gQ = torch.empty(tuple(w.Q.shape), dtype=torch.float32, device=dev)
+            self.gD = torch.empty(tuple(w.D.shape), dtype=torch.float32, device=dev)
+        p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        self.p = p
+        self.lay = lay
+
+    def stream(self):
+        return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+    def fwd(self):
+        p, L = self.p, self.L
+        Nq, Lq, Nx, Ld, dim = self.dims
+        if self.lay == "allpairs":
+            st = L.lik_maxsim_fwd(p(self.Q), p(self.D), self.dt, Nq, Lq, Nx, Ld, dim, p(self.qm),
+                                  p(self.dm), p(self.scores), p(self.argmax), p(self.wsf),
+                                  self.wsf_n, self.stream())
+        elif self.lay == "pairwise":
+            st = L.lik_maxsim_pairwise_fwd(p(self.Q), p(self.D), self.dt, Nq, Lq, Ld, dim,
+                                           p(self.qm), p(self.dm), p(self.scores), p(self.argmax),
+                                           p(self.wsf), self.wsf_n, self.stream())
+        else:
+            st = L.lik_maxsim_kd_fwd(p(self.Q), p(self.D), self.dt, Nq, Lq, Nx, Ld, dim,
+                                     p(self.qm), p(self.dm), p(self.scores), p(self.argmax),
+                                     p(self.wsf), self.wsf_n, self.stream())
+        if st != 0:
+            raise RuntimeError(f"forward failed: {L.lik_last_error().decode()}")
+
+    def bwd(self):
+        p, L = self.p, self.L
+        Nq, Lq, Nx, Ld, dim = self.dims
+        args = (p(self.qm), p(self.dm), p(self.g), p(self.argmax), p(self.gQ), p(self.gD),
+                p(self.wsb), self.wsb_n, self.stream())
+        if self.lay == "allpairs":
+            st = L.lik_maxsim_bwd(p(self.Q), p(self.D), self.dt, Nq, Lq, Nx, Ld, dim, *args)
+        elif self.lay == "pairwise":
+            st = L.lik_maxsim_pairwise_bwd(p(self.Q), p(self.D), self.dt, Nq, Lq, Ld, dim, *args)
+        else:
+            st = L.lik_maxsim_kd_bwd(p(self.Q), p(self.D), self.dt, Nq, Lq, Nx, Ld, dim, *args)
+        if st != 0:
+            raise RuntimeError(f"backward failed: {L.lik_last_error().decode()}")
+
+
+# --------------------------------------------------------------------------
+# measured HBM traffic recorded from rocprofv3 counters
+# --------------------------------------------------------------------------
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "maxsim_scoring_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """Bytes per launch of `kernel` from profiles/traffic_<kernel>_<workload>.md,
+    or None when absent or taken from different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"bytes_per_launch:\s*([0-9.eE+]+)", text)
+    d = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not d or d.group(1) != kernel_source_digest():
+        return None
+    return float(m.group(1))
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def make_workload(name: str):
+    from maxsim_scoring_02_amd import workloads as wl
+
+    if name == "inbatch-text":
+        return wl.inbatch_text(), True
+    if name == "inbatch-pages":
+        w = wl.inbatch_pages()
+        # upstream grad of the cross-entropy over the diagonal, from the
+        # scores of the forward itself (formed once, outside the timed steps)
+        import torch
+        op = Op(w, backward=False)
+        op.fwd()
+        torch.cuda.synchronize()
+        w.grad = torch.from_numpy(wl.ce_diag_grad(op.scores.cpu().numpy()))
+        return w, True
+    if name == "kd-candidates":
+        return wl.kd_candidates(), True
+    if name == "long-docs":
+        return wl.long_docs(), False
+    if name == "long-rerank":
+        return wl.long_rerank(), False
+    raise SystemExit(f"unknown workload {name}")
+
+
+DOMINANT = {  # kernel whose roofline is reported, and its bound
+    "inbatch-text": ("allpairs_fwd", "mfma"),
+    "inbatch-pages": ("allpairs_fwd", "mfma"),
+    "long-docs": ("allpairs_fwd", "mfma"),
+    "kd-candidates": ("pairs_fwd", "hbm"),
+    "long-rerank": ("pairs_fwd", "hbm"),
+}
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# --------------------------------------------------------------------------
+
+def cpu_baseline(w, backward: bool, budget_s: float = 12.0):
+    import oracle
+    from maxsim_scoring_02_amd.workloads import Workload
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores = _threads()
+    Qn, Dn, qm, dm = w.numpy_inputs()
+    g = None if w.grad is None else w.grad.numpy()
+    lay = w.layout
+    # sample: the first n queries (all-pairs: against every document; pairs:
+    # their own documents), growing n until the budget is used
+    n_total = Qn.shape[0]
+    n = 1
+    spent, flops = 0.0, 0.0
+
+    def run(k):
+        sub_q = slice(0, k)
+        Qs = Qn[sub_q]
+        qms = None if qm is None else qm[sub_q]
+        if lay == "allpairs":
+            Ds, dms = Dn, dm
+            gs = None if g is None else g[sub_q]
+            fw, bw = oracle.maxsim_allpairs, oracle.maxsim_allpairs_bwd
+        else:
+            Ds = Dn[sub_q]
+            dms = None if dm is None else dm[sub_q]
+            gs = None if g is None else g[sub_q]
+            fw = oracle.maxsim_pairwise if lay == "pairwise" else oracle.maxsim_kd
+            bw = oracle.maxsim_pairwise_bwd if lay == "pairwise" else oracle.maxsim_kd_bwd
+        t0 = time.perf_counter()
+        r = fw(Qs, Ds, qms, dms)
+        if backward:
+            bw(Qs, Ds, gs, r.argmax, qms, dms)
+        dt = time.perf_counter() - t0
+        import torch
+        sub = Workload(w.name, lay, w.dtype, torch.from_numpy(Qs), torch.from_numpy(Ds),
+                       None if qms is None else torch.from_numpy(qms),
+                       None if dms is None else torch.from_numpy(dms), None)
+        f = work(sub)
+        return dt, (f[0] + (f[1] if backward else 0.0)), (f[2] + (f[3] if backward else 0.0))
+
+    ctx = threadpool_limits(cores) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        while True:
+            dt, fl, by = run(n)
+            if dt >= 0.6 * budget_s or n >= n_total:
+                break
+            n = min(n_total, max(n + 1, int(n * min(8.0, budget_s / max(dt, 1e-3)))))
+        spent, flops, nbytes = dt, fl, by
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    what = ("fwd+bwd" if backward else "fwd")
+    sample = (f"{what} of the first {n} of {n_total} queries"
+              + (" against all documents" if lay == "allpairs" else " with their documents"))
+    return spent, flops, nbytes, cores, sample
+
+
+# --------------------------------------------------------------------------
+# main
+# --------------------------------------------------------------------------
+
+def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None):
+    import torch
+
+    w, backward = make_workload(name)
+    op = Op(w, backward)
+    f_fwd, f_bwd, b_fwd, b_bwd = work(w)
+    for _ in range(warmup):
+        op.fwd()
+        if backward:
+            op.bwd()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(E(), E(), E()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        op.fwd()
+        e1.record()
+        if backward:
+            op.bwd()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+    span_ms = ev[0][0].elapsed_time(ev[-1][2])
+    ms_step = span_ms / steps
+    t_fwd = float(np.mean(fwd_ms))
+    t_bwd = float(np.mean(bwd_ms)) if backward else 0.0
+    kern, bound = DOMINANT[name]
+    if bound == "mfma":
+        flops = f_fwd + (f_bwd if backward else 0.0)
+        value = flops / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = f_fwd / (t_fwd * 1e-3) / 1e12
+        peak = PEAK_MFMA_16BIT
+        rl_unit = "TFLOP/s"
+    else:
+        nbytes = b_fwd + (b_bwd if backward else 0.0)
+        value = nbytes / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = b_fwd / (t_fwd * 1e-3) / 1e9
+        peak = PEAK_HBM
+        rl_unit = "GB/s"
+    traffic = recorded_traffic(name, kern)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes of the pages' workloads)",
+        "config": {
+            "workload": name,
+            "layout": w.layout,
+            "Q": list(w.Q.shape),
+            "D": list(w.D.shape),
+            "backward": backward,
+            "fwd_ms": round(t_fwd, 5),
+            "bwd_ms": round(t_bwd, 5),
+            "fwd_flops_valid": f_fwd,
+            "bwd_flops_valid": f_bwd,
+            "fwd_bytes": b_fwd,
+            "bwd_bytes": b_bwd,
+            "wall_s_timed": round(wall, 4),
+        },
+        "roofline": {
+            "bound": bound,
+            "kernel": kern,
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": rl_unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "timed_as": "forward entry point (mask prep + main kernel), HIP events",
+        },
+        "cpu_baseline": None,
+    }
+    if dump_dir:
+        np.save(os.path.join(dump_dir, f"{name}_scores.npy"), op.scores.cpu().numpy())
+    if with_cpu:
+        spent, fl, nb, cores, sample = cpu_baseline(w, backward)
+        if bound == "mfma":
+            cv, cu = fl / spent / 1e12, "TFLOP/s"
+        else:
+            cv, cu = nb / spent / 1e9, "GB/s"
+        line["cpu_baseline"] = {"value": round(cv, 6), "unit": cu, "cores": cores,
+                                "kind": "oracle", "sample": sample,
+                                "seconds": round(spent, 3)}
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="inbatch-text")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this operator build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    names = (["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"]
+             if args.workload == "all" else [args.workload])
+    for i, name in enumerate(names):
+        line = bench_one(name, args.steps, args.warmup,
+                         with_cpu=(not args.no_cpu_baseline))
+        print(json.dumps(line), flush=True)
+        if i + 1 < len(names):
+            torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()
