@@ -31,6 +31,8 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # keep hand-written float code off packed-FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the epilogue reads them with plain VALU ops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -12,7 +12,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/lik.h"
+#include "lik.h"
 #include "lik_kernels.h"
 #include "lik_plan.h"
 

@@ -21,6 +21,9 @@
 
 namespace lik {
 
+// documents up to this length use the per-wave histogram sort (4 * Ld ints of LDS)
+constexpr int64_t kSortWavesMaxLd = 3840;
+
 struct BwdArgs {
   const void* Q;
   const void* D;
@@ -28,7 +31,8 @@ struct BwdArgs {
   const int32_t* argmax;
   float* gQ;
   float* gD;
-  int32_t* sorted;   // [n_docs][H] hit ids ordered by row, then by hit id
+  int32_t* sorted;   // [n_docs][H] Q-row index of each hit, ordered by doc row, then hit id
+  float* sorted_g;   // [n_docs][H] upstream gradient g[pair] of each sorted hit
   int32_t* roff;     // [n_docs][Ld + 1] row offsets into `sorted`
   int layout;
   int key_bits;
@@ -55,7 +59,9 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
   float acc[EPC];
 #pragma unroll
   for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-  constexpr int U = 4;
+  // 16 gathered rows in flight per thread: the loop is bound by memory
+  // latency, not bandwidth, at the usual few-thousand-thread grids
+  constexpr int U = 16;
   for (int64_t k0 = 0; k0 < K; k0 += U) {
     int jj[U];
     float gg[U];
@@ -96,6 +102,84 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// grad_Q, sliced: one workgroup per (query, token); its threads are CPR
+// chunk lanes x NS document slices.  Every thread gathers its slice's rows
+// with all loads independent (one latency round trip for the indices, one
+// for the rows), and the NS slice partials of each chunk are added in slice
+// order through LDS: deterministic, and tens of thousands of rows in flight.
+// ---------------------------------------------------------------------------
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void gradq_sliced_kernel(BwdArgs a) {
+  using G = Geo<E, DIM>;
+  constexpr int EPC = ElemInfo<E>::kPerChunk;
+  constexpr int CPR = G::kCPR;
+  constexpr int NS = 256 / CPR;            // document slices
+  constexpr int U = 16;                    // rows per round
+  __shared__ float part[NS][CPR * EPC];
+  const int tid = threadIdx.x;
+  const int c = tid % CPR, sl = tid / CPR;
+  const int64_t qi = blockIdx.x;           // q * Lq + i
+  const int64_t q = qi / a.Lq, i = qi - q * a.Lq;
+  const bool ap = a.layout == kAllPairs;
+  const int64_t K = ap ? a.n_docs : a.K;
+  const int64_t per = (K + NS - 1) / NS;
+  const int64_t k_lo = min(sl * per, K), k_hi = min(k_lo + per, K);
+  const char* Db = (const char*)a.D;
+  float acc[EPC];
+#pragma unroll
+  for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
+  for (int64_t k0 = k_lo; k0 < k_hi; k0 += U) {
+    int jj[U];
+    float gg[U];
+    int64_t dd[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u;
+      jj[u] = -1;
+      gg[u] = 0.0f;
+      dd[u] = 0;
+      if (k < k_hi) {
+        const int64_t p = q * K + k;
+        dd[u] = ap ? k : p;
+        jj[u] = a.argmax[p * a.Lq + i];
+        gg[u] = a.g[p];
+      }
+    }
+    u32x4 ch[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = jj[u] >= 0 && jj[u] < a.Ld;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      ch[u] = ok ? ld_global_16(Db + (dd[u] * a.Ld + jj[u]) * (int64_t)G::kRowBytes + c * 16) : z;
+      if (!ok) gg[u] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[EPC];
+      chunk_to_float<E>(ch[u], f);
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[u], f[k], acc[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < EPC; ++k) part[sl][c * EPC + k] = acc[k];
+  __syncthreads();
+  // thread t < CPR*EPC/4 sums one float4 of the row over the slices in order
+  constexpr int NV = CPR * EPC / 4;
+  if (tid < NV) {
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x = 0; x < NS; ++x) {
+      const float4 v = *reinterpret_cast<const float4*>(&part[x][tid * 4]);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    *reinterpret_cast<float4*>(a.gQ + qi * DIM + tid * 4) = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // grad_D, step 1: per document, hits sorted by row (stable)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int hit_row(const BwdArgs& a, int64_t e, int64_t h) {
@@ -110,6 +194,18 @@ __device__ __forceinline__ int hit_row(const BwdArgs& a, int64_t e, int64_t h) {
   }
   const int j = a.argmax[p * a.Lq + i];
   return (j >= 0 && j < a.Ld) ? j : -1;
+}
+
+// Q row and score (pair) index of hit h of document e.
+__device__ __forceinline__ void hit_qrow_pair(const BwdArgs& a, int64_t e, int64_t h,
+                                              int64_t& qrow, int64_t& p) {
+  if (a.layout == kAllPairs) {
+    qrow = h;
+    p = (h / a.Lq) * a.n_docs + e;
+  } else {
+    qrow = (e / a.K) * a.Lq + h;
+    p = e;
+  }
 }
 
 __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
@@ -173,7 +269,12 @@ __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
         const int count = __popcll(same);
         const int pos = v ? cur[j] : 0;
         __asm__ volatile("" ::: "memory");
-        if (v && pos + rank < H) out[pos + rank] = (int32_t)h;
+        if (v && pos + rank < H) {
+          int64_t qrow, p;
+          hit_qrow_pair(a, e, h, qrow, p);
+          out[pos + rank] = (int32_t)qrow;
+          a.sorted_g[e * H + pos + rank] = a.g[p];
+        }
         if (v && rank == count - 1) cur[j] = pos + count;
       }
       __syncthreads();
@@ -244,6 +345,258 @@ __global__ __launch_bounds__(256) void gradd_rows_kernel(BwdArgs a) {
     *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
 }
 
+// ---------------------------------------------------------------------------
+// grad_D, step 1 (parallel form): each of the 4 waves owns a contiguous
+// quarter of the document's hits and its own row histogram, so the stable
+// placement needs no cross-wave turns: a hit's slot is the row's start, plus
+// the row's hits in earlier waves, plus its ballot rank inside its wave.
+// LDS: 4 * Ld + 4 ints.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gradd_sort_waves_kernel(BwdArgs a) {
+  extern __shared__ int smem[];
+  const int Ld = (int)a.Ld;
+  int* cnt = smem;               // [4][Ld] counts, then running cursors
+  int* wtot = smem + 4 * Ld;     // 4 wave totals of the scan
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t e = blockIdx.x;
+  const int64_t H = a.H;
+  const int64_t Hq = ((H + 255) / 256) * 64;   // hits per wave, a multiple of 64
+  const int64_t h0 = min(wave * Hq, H), h1 = min(h0 + Hq, H);
+
+  for (int j = tid; j < 4 * Ld; j += 256) cnt[j] = 0;
+  __syncthreads();
+  int* mine = cnt + wave * Ld;
+  // 16 independent argmax loads in flight per lane before any is consumed
+  constexpr int UH = 16;
+  for (int64_t hb = h0 + lane; hb < h1; hb += 64 * UH) {
+    int jj[UH];
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+      const int64_t h = hb + 64 * u;
+      jj[u] = h < h1 ? hit_row(a, e, h) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < UH; ++u)
+      if (jj[u] >= 0) atomicAdd(&mine[jj[u]], 1);
+  }
+  __syncthreads();
+
+  // exclusive scan over rows of the per-row totals; per-wave cursors
+  const int seg = (Ld + 255) / 256;
+  const int lo = min(tid * seg, Ld), hi = min(lo + seg, Ld);
+  int local = 0;
+  for (int j = lo; j < hi; ++j) local += cnt[j] + cnt[Ld + j] + cnt[2 * Ld + j] + cnt[3 * Ld + j];
+  int incl = local;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int t = __shfl_up(incl, k);
+    if (lane >= k) incl += t;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = incl - local;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  int32_t* roff = a.roff + e * (a.Ld + 1);
+  for (int j = lo; j < hi; ++j) {
+    roff[j] = base;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = cnt[w * Ld + j];
+      cnt[w * Ld + j] = base;
+      base += c;
+    }
+  }
+  if (tid == 0) roff[Ld] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  __syncthreads();
+
+  int32_t* out = a.sorted + e * H;
+  float* outg = a.sorted_g + e * H;
+  const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  // rows of the next chunk of 64 hits are loaded while this chunk is placed
+  int jn = (h0 + lane < h1) ? hit_row(a, e, h0 + lane) : -1;
+  for (int64_t hb = h0; hb < h1; hb += 64) {
+    const int64_t h = hb + lane;
+    const int j = jn;
+    jn = (hb + 64 + lane < h1) ? hit_row(a, e, hb + 64 + lane) : -1;
+    const bool v = j >= 0;
+    uint64_t same = __ballot(v);
+    for (int b = 0; b < a.key_bits; ++b) {
+      const bool bit = v && ((j >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(same & below);
+    const int count = __popcll(same);
+    const int pos = v ? mine[j] : 0;
+    __asm__ volatile("" ::: "memory");
+    if (v && pos + rank < H) {
+      int64_t qrow, p;
+      hit_qrow_pair(a, e, h, qrow, p);
+      out[pos + rank] = (int32_t)qrow;
+      outg[pos + rank] = a.g[p];
+    }
+    if (v && rank == count - 1) mine[j] = pos + count;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grad_D, step 2 (wave per row): the wave's lanes form 64/CPR entry groups;
+// group k takes the row's entries k, k + groups, ... (in sorted order) and the
+// group partials are added by a fixed xor tree, so the sum order depends only
+// on the row's entry list: deterministic, and long rows are spread over the
+// whole wave.  Each wave walks `rpw` consecutive rows.
+// ---------------------------------------------------------------------------
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void gradd_rows_wave_kernel(BwdArgs a, int rpw) {
+  using G = Geo<E, DIM>;
+  constexpr int EPC = ElemInfo<E>::kPerChunk;
+  constexpr int CPR = G::kCPR;
+  constexpr int EG = CPR >= 64 ? 1 : 64 / CPR;    // entry groups per wave
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = CPR >= 64 ? 0 : lane / CPR, c = CPR >= 64 ? lane : lane - grp * CPR;
+  const int64_t n_rows = a.n_docs * a.Ld;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * rpw;
+  const bool ap = a.layout == kAllPairs;
+  const char* Qb = (const char*)a.Q;
+  for (int rr = 0; rr < rpw; ++rr) {
+    const int64_t row = row0 + rr;
+    if (row >= n_rows) break;
+    const int64_t e = row / a.Ld;
+    const int64_t j = row - e * a.Ld;
+    const int32_t* roff = a.roff + e * (a.Ld + 1);
+    const int s = max(0, min(roff[j], (int)a.H));
+    const int t = max(s, min(roff[j + 1], (int)a.H));
+    const int32_t* lst = a.sorted + e * a.H;
+    float acc[EPC];
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
+    for (int k0 = s; k0 < t; k0 += EG * U) {
+      float gg[U];
+      int64_t qrow[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * EG + grp;
+        gg[u] = 0.0f;
+        qrow[u] = 0;
+        if (k < t) {
+          const int64_t h = min(max((int64_t)lst[k], (int64_t)0), a.H - 1);
+          int64_t p;
+          if (ap) {
+            const int64_t q = h / a.Lq;
+            p = q * a.n_docs + e;
+            qrow[u] = h;
+          } else {
+            p = e;
+            qrow[u] = (e / a.K) * a.Lq + h;
+          }
+          gg[u] = a.g[p];
+        }
+      }
+      u32x4 ch[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        ch[u] = ld_global_16(Qb + qrow[u] * (int64_t)G::kRowBytes + c * 16);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float f[EPC];
+        chunk_to_float<E>(ch[u], f);
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[u], f[k], acc[k]);
+      }
+    }
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) acc[k] += __shfl_xor(acc[k], off);
+    if (grp == 0) {
+      float* out = a.gD + row * DIM + c * EPC;
+#pragma unroll
+      for (int k = 0; k < EPC; k += 4)
+        *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grad_D, step 2 (lane group per row): a group of CPR lanes (one 16-byte
+// chunk of the row each) owns `rpg` consecutive rows.  The rows' offsets come
+// in one load; a row's (Q row, g) pairs come 16 at a time, the next 16
+// prefetched while the current 16 Q rows are in flight; partial sums are
+// added in the sorted order, so every row has one owner and a fixed order.
+// ---------------------------------------------------------------------------
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void gradd_rows_group_kernel(BwdArgs a, int rpg) {
+  using G = Geo<E, DIM>;
+  constexpr int EPC = ElemInfo<E>::kPerChunk;
+  constexpr int CPR = G::kCPR;                  // lanes per group
+  constexpr int GPB = 256 / CPR;                // groups per workgroup
+  constexpr int B = CPR < 16 ? CPR : 16;        // entries per batch (one pair per lane)
+  const int tid = threadIdx.x;
+  const int c = tid % CPR;
+  const int64_t gid = (int64_t)blockIdx.x * GPB + tid / CPR;
+  const int64_t n_rows = a.n_docs * a.Ld;
+  const int64_t row0 = gid * rpg;
+  if (row0 >= n_rows) return;
+  const char* Qb = (const char*)a.Q;
+  // lane c < rpg: offsets [s, t) of row row0 + c
+  int my_s = 0, my_t = 0;
+  if (c < rpg && row0 + c < n_rows) {
+    const int64_t row = row0 + c;
+    const int64_t e = row / a.Ld, j = row - e * a.Ld;
+    const int32_t* roff = a.roff + e * (a.Ld + 1);
+    my_s = max(0, min(roff[j], (int)a.H));
+    my_t = max(my_s, min(roff[j + 1], (int)a.H));
+  }
+  for (int r = 0; r < rpg; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= n_rows) break;
+    const int s = __shfl(my_s, r, CPR), t = __shfl(my_t, r, CPR);
+    const int64_t e = row / a.Ld;
+    const int32_t* lq = a.sorted + e * a.H;
+    const float* lg = a.sorted_g + e * a.H;
+    float acc[EPC];
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
+    // pairs of the first batch
+    int pq = 0;
+    float pg = 0.0f;
+    if (s + c < t && c < B) {
+      pq = lq[s + c];
+      pg = lg[s + c];
+    }
+    for (int k0 = s; k0 < t; k0 += B) {
+      const int cq = pq;
+      const float cg = pg;
+      // prefetch the next batch's pairs
+      if (k0 + B + c < t && c < B) {
+        pq = lq[k0 + B + c];
+        pg = lg[k0 + B + c];
+      }
+      const int nb = min(B, t - k0);
+      u32x4 ch[B];
+      float gg[B];
+#pragma unroll
+      for (int m = 0; m < B; ++m) {
+        const int64_t qrow = min(max(__shfl(cq, m, CPR), 0), (int)(a.Nq * a.Lq) - 1);
+        gg[m] = m < nb ? __shfl(cg, m, CPR) : 0.0f;
+        ch[m] = ld_global_16(Qb + qrow * (int64_t)G::kRowBytes + c * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < B; ++m) {
+        float f[EPC];
+        chunk_to_float<E>(ch[m], f);
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[m], f[k], acc[k]);
+      }
+    }
+    float* out = a.gD + row * DIM + c * EPC;
+#pragma unroll
+    for (int k = 0; k < EPC; k += 4)
+      *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+  }
+}
+
 __global__ void zero_kernel(float4* p, int64_t n4) {
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k < n4) p[k] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -263,20 +616,39 @@ static hipError_t launch_grads(const BwdArgs& a, bool want_q, bool want_d, hipSt
   using G = Geo<E, DIM>;
   constexpr int CPR = G::kCPR;
   if (want_q) {
-    const int64_t tpb = 256 / CPR;
-    hipLaunchKernelGGL((gradq_kernel<E, DIM>), dim3((unsigned)a.Nq, (unsigned)cdiv(a.Lq, tpb)),
-                       dim3(256), 0, s, a);
+    const int64_t K = a.layout == kAllPairs ? a.n_docs : a.K;
+    if (K >= 64) {
+      // many documents per query: split each (query, token) over slices
+      hipLaunchKernelGGL((gradq_sliced_kernel<E, DIM>), dim3((unsigned)(a.Nq * a.Lq)), dim3(256), 0,
+                         s, a);
+    } else {
+      const int64_t tpb = 256 / CPR;
+      hipLaunchKernelGGL((gradq_kernel<E, DIM>), dim3((unsigned)a.Nq, (unsigned)cdiv(a.Lq, tpb)),
+                         dim3(256), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (want_d) {
-    const size_t lds = (size_t)(a.Ld + 4) * sizeof(int);
-    hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (a.Ld <= kSortWavesMaxLd) {
+      const size_t lds = (size_t)(4 * a.Ld + 4) * sizeof(int);
+      hipLaunchKernelGGL(gradd_sort_waves_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
+    } else {
+      const size_t lds = (size_t)(a.Ld + 4) * sizeof(int);
+      hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t rpb = 256 / CPR;
-    hipLaunchKernelGGL((gradd_rows_kernel<E, DIM>), dim3((unsigned)cdiv(a.n_docs * a.Ld, rpb)),
-                       dim3(256), 0, s, a);
+    // rows per group: one while groups are scarce; up to 16 (one offsets
+    // load) when the output is large and mostly empty rows
+    const int64_t n_rows = a.n_docs * a.Ld;
+    int rpg = (int)cdiv(n_rows, 256 * 256);
+    const int max_rpg = CPR < 16 ? CPR : 16;   // one offsets load per group
+    rpg = rpg < 1 ? 1 : (rpg > max_rpg ? max_rpg : rpg);
+    const int64_t gpb = 256 / CPR;
+    hipLaunchKernelGGL((gradd_rows_group_kernel<E, DIM>),
+                       dim3((unsigned)cdiv(cdiv(n_rows, rpg), gpb)), dim3(256), 0, s, a, rpg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -322,6 +694,7 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
   a.gQ = grad_Q;
   a.gD = grad_D;
   a.sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
+  a.sorted_g = reinterpret_cast<float*>(ws + p.off_sorted_g);
   a.roff = reinterpret_cast<int32_t*>(ws + p.off_roff);
   a.layout = f.layout;
   a.key_bits = p.key_bits;

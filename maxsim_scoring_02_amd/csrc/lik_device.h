@@ -113,30 +113,110 @@ __device__ __forceinline__ void state_init(BlockState& s, int t0) {
   for (int v = 0; v < 16; ++v) s.best_val[v] = -__builtin_inff();
 }
 
-// Fold one tile's accumulator into the running state.  `word` masks rows
-// (masked rows never win).  Strict '>' keeps the earlier tile on ties.
-__device__ __forceinline__ void state_update(BlockState& s, f32x16 acc, uint32_t word, int t, int h) {
-  if (word != 0xffffffffu) {
-    uint32_t w = word >> (4 * h);
+// Masked rows of a tile never win: set them to -inf.  `word` bit r = row r
+// valid.  Call only for tiles that are not fully valid.
+__device__ __forceinline__ void tile_mask(f32x16& acc, uint32_t word, int h) {
+  const uint32_t w = word >> (4 * h);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      int bit = 8 * (v >> 2) + (v & 3);
-      if (!((w >> bit) & 1u)) acc[v] = -__builtin_inff();
-    }
+  for (int v = 0; v < 16; ++v) {
+    const int bit = 8 * (v >> 2) + (v & 3);
+    if (!((w >> bit) & 1u)) acc[v] = -__builtin_inff();
   }
-  float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
-  float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
-  float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
-  float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
-  float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
-  float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
-  float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
-  float tmax = __builtin_fmaxf(m1, m2);
-  bool better = tmax > s.run_max;
+}
+
+// Fold one (masked) tile's accumulator into the running state, branch-free.
+// Strict '>' keeps the earlier tile on ties, so tiles must come in order.
+__device__ __forceinline__ void state_fold(BlockState& s, const f32x16& acc, int t) {
+  const float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
+  const float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
+  const float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
+  const float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
+  const float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
+  const float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
+  const float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
+  const float tmax = __builtin_fmaxf(m1, m2);
+  const bool better = tmax > s.run_max;
   s.run_max = better ? tmax : s.run_max;
   s.best_tile = better ? t : s.best_tile;
 #pragma unroll
   for (int v = 0; v < 16; ++v) s.best_val[v] = better ? acc[v] : s.best_val[v];
+}
+
+// Padded LDS layout: each document row takes its bytes plus 16, so the 32
+// rows read by one MFMA operand load start 4 banks apart (no conflicts), and
+// a lane's successive K-step chunks sit at fixed immediate offsets.
+template <Elem E, int DIM>
+struct Pad {
+  static constexpr int kStride = Geo<E, DIM>::kRowBytes + 16;
+  static constexpr int kTileBytes = kTile * kStride;
+};
+
+// Mask the rows of a tile that are not valid (-inf never wins a max).  The
+// per-element row validity is computed once and applied to all NB blocks.
+template <int NB>
+__device__ __forceinline__ void tiles_mask(f32x16 (&acc)[NB], uint32_t word, int h) {
+  const uint32_t w = word >> (4 * h);
+  bool ok[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ok[v] = (w >> (8 * (v >> 2) + (v & 3))) & 1u;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = ok[v] ? acc[b][v] : -__builtin_inff();
+}
+
+// Fold a masked tile into the running state.  The copy of the tile's values
+// runs only in the lanes whose maximum improved (strict '>': the earlier tile
+// keeps ties), and is skipped by the whole wave when no lane improved.
+__device__ __forceinline__ void state_fold_sparse(BlockState& s, const f32x16& acc, int t) {
+  const float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
+  const float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
+  const float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
+  const float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
+  const float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
+  const float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
+  const float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
+  const float tmax = __builtin_fmaxf(m1, m2);
+  if (tmax > s.run_max) {
+    s.run_max = tmax;
+    s.best_tile = t;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s.best_val[v] = acc[v];
+  }
+}
+
+// Leaner state: the running max and the absolute doc row that reached it
+// (lowest row on ties), resolved inside each tile as it is folded.
+struct RowState {
+  float run_max;
+  int best_row;
+};
+
+__device__ __forceinline__ void rowstate_init(RowState& s) {
+  s.run_max = -__builtin_inff();
+  s.best_row = 0;
+}
+
+__device__ __forceinline__ void rowstate_fold(RowState& s, const f32x16& acc, int t, int h) {
+  const float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
+  const float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
+  const float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
+  const float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
+  const float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
+  const float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
+  const float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
+  const float tmax = __builtin_fmaxf(m1, m2);
+  int kk = 15;
+#pragma unroll
+  for (int v = 14; v >= 0; --v) kk = (acc[v] == tmax) ? v : kk;
+  const bool better = tmax > s.run_max;
+  s.run_max = better ? tmax : s.run_max;
+  s.best_row = better ? t * kTile + acc_row(kk, h) : s.best_row;
+}
+
+__device__ __forceinline__ void state_update(BlockState& s, f32x16 acc, uint32_t word, int t, int h) {
+  if (word != 0xffffffffu) tile_mask(acc, word, h);
+  state_fold(s, acc, t);
 }
 
 // (max, lowest doc row reaching it) of this lane's half-column.

@@ -96,15 +96,53 @@ __device__ __forceinline__ void load_bfrags(u32x4 (&bf)[NB][KS], const char* Qb,
 
 // ---------------------------------------------------------------------------
 // all-pairs forward
+//
+// A workgroup of 4 waves holds 4 x SPW query-token slots in registers (the
+// MFMA B operand) and streams document super-tiles of 2 x 32 rows through a
+// double-buffered LDS ring (padded rows), one barrier per super-tile.  Tiles
+// arrive by buffer loads whose descriptor covers only the unit's remaining
+// rows, so rows past the end read as zeros (and are masked) with no per-lane
+// bounds arithmetic.  Two workgroups fit on a CU, so the waves sharing a SIMD
+// run in independent phases and one's MFMAs overlap the other's VALU work.
 // ---------------------------------------------------------------------------
-constexpr int kApNW = 8;                       // waves per workgroup
+constexpr int kApNW = 4;                       // waves per workgroup
 constexpr int kApThreads = kApNW * kWave;
+constexpr int kSub = 2;                        // tiles per super-tile
+
+template <Elem E, int DIM>
+constexpr int ap_lds_bytes() {
+  return 2 * kSub * Pad<E, DIM>::kTileBytes;
+}
 
 template <Elem E, int DIM, int NB>
+__device__ __forceinline__ void mfma_tile_pad(f32x16 (&acc)[NB], const char* buf,
+                                              const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
+                                              int a_off) {
+  using G = Geo<E, DIM>;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+#pragma unroll
+  for (int m = 0; m < G::kKSteps; ++m) {
+    const u32x4 av = ld_lds_16(buf, a_off + m * 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mfma_chunk<E>(acc[b], av, bf[b][m]);
+  }
+}
+
+template <Elem E, int DIM, int NB, bool MASK>
 __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   using G = Geo<E, DIM>;
+  using PD = Pad<E, DIM>;
   constexpr int SPW = 32 * NB;
-  constexpr int kLoads = (G::kTileChunks + kApThreads - 1) / kApThreads;
+  constexpr int kSTRows = kSub * kTile;
+  constexpr int kSTBytes = kSub * PD::kTileBytes;
+  constexpr int kSTChunks = kSTRows * G::kCPR;
+  constexpr int kLoads = kSTChunks / kApThreads;
+  constexpr int kRowsPerLoad = kApThreads / G::kCPR;       // rows one load step covers
+  constexpr int kBytesPerLoad = kApThreads * 16;
+  static_assert(kSTChunks % kApThreads == 0 && kApThreads % G::kCPR == 0,
+                "super-tile chunks must split evenly over the workgroup");
+  constexpr uint32_t kFull = 0xffffffffu;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
@@ -113,12 +151,13 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give every doc
   // group a fixed XCD so its tiles stay in that XCD's L2 across slot blocks.
-  const int64_t bid = blockIdx.x;
-  const int64_t xcd = bid & 7, kx = bid >> 3;
-  const int64_t g = xcd + 8 * (kx % a.gpx);
-  const int64_t sb = kx / a.gpx;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, kx = bid >> 3;
+  const int gpx = (int)a.gpx;
+  const int g = xcd + 8 * (kx % gpx);
+  const int sb = kx / gpx;
   if (g >= a.n_groups || sb >= a.n_sb) return;
-  const int64_t gw = sb * kApNW + wave;
+  const int gw = sb * kApNW + wave;
   const bool active = gw < a.n_cg;
 
   // query fragments of this wave's slots (B operand), kept for all units
@@ -134,57 +173,82 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     }
     load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
   }
+  // this lane's output slot, fixed for the whole kernel
+  const int L = NB == 2 ? lane : (lane & 31);
+  const bool writer = NB == 2 || lane < 32;
+  int64_t slot_q = 0, slot_i = 0;
+  const bool slot_ok = active && slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, slot_q, slot_i);
+  const bool slot_tok = slot_ok && (!a.q_mask || a.q_mask[slot_q * a.Lq + slot_i]);
+  const int seg_start = a.qpw > 0 ? (int)((L / a.Lq) * a.Lq) : 0;
+  const bool seg_last = slot_ok && slot_i == a.Lq - 1;
 
+  // Units u = d * nchunks + c of this workgroup: [u_begin, u_end).  (d, c)
+  // are stepped incrementally; tile counts are uniform (readfirstlane).
+  const int nchunks = (int)a.nchunks, tpc = (int)a.tpc;
   const int64_t n_units = a.n_docs * a.nchunks;
-  const int64_t u_begin = g * a.upw;
-  const int64_t u_end = min(u_begin + a.upw, n_units);
-  const int64_t ntiles_full = a.ntiles_max;
-
-  auto unit_tiles = [&](int64_t u, int64_t& d, int64_t& t0, int64_t& t1) {
-    d = u / a.nchunks;
-    const int64_t c = u - d * a.nchunks;
-    const int64_t nt = a.ntiles ? (int64_t)a.ntiles[d] : ntiles_full;
-    t0 = c * a.tpc;
-    t1 = min(t0 + a.tpc, nt);
+  const int64_t u_begin = (int64_t)g * a.upw;
+  const int n_my = (int)(min(u_begin + a.upw, n_units) - u_begin);
+  const int d_begin = (int)(u_begin / nchunks), c_begin = (int)(u_begin % nchunks);
+  const int ntiles_full = (int)a.ntiles_max;
+  auto doc_tiles = [&](int d) -> int {
+    return MASK ? __builtin_amdgcn_readfirstlane(a.ntiles[d]) : ntiles_full;
+  };
+  auto chunk_range = [&](int nt, int c, int& t0, int& t1) {
+    t0 = c * tpc;
+    t1 = min(t0 + tpc, nt);
     if (t1 < t0) t1 = t0;
   };
 
-  // load cursor: the next tile to bring into LDS, in consumption order
-  int64_t pu = u_begin, pd = 0, pt = 0, pt1 = 0;
+  // load cursor: the next super-tile to bring into LDS, in consumption order
+  int pk = 0, pd = d_begin, pc = c_begin, pnt = doc_tiles(d_begin), pt = 0, pt1 = 0;
   bool have = false;
-  for (; pu < u_end; ++pu) {
-    unit_tiles(pu, pd, pt, pt1);
+  for (; pk < n_my;) {
+    chunk_range(pnt, pc, pt, pt1);
     if (pt < pt1) { have = true; break; }
+    ++pk;
+    if (++pc == nchunks) { pc = 0; ++pd; if (pk < n_my) pnt = doc_tiles(pd); }
   }
+  // When nothing follows, the cursor stays on the last super-tile (the
+  // prefetch then re-reads it from L2 and the copy is not stored).
   auto advance = [&]() {
-    ++pt;
-    if (pt < pt1) return true;
-    for (++pu; pu < u_end; ++pu) {
-      unit_tiles(pu, pd, pt, pt1);
-      if (pt < pt1) return true;
+    if (pt + kSub < pt1) {
+      pt += kSub;
+      return true;
+    }
+    int k = pk, d = pd, c = pc, nt = pnt;
+    while (k + 1 < n_my) {
+      ++k;
+      if (++c == nchunks) { c = 0; ++d; nt = doc_tiles(d); }
+      int t0, t1;
+      chunk_range(nt, c, t0, t1);
+      if (t0 < t1) {
+        pk = k; pd = d; pc = c; pnt = nt; pt = t0; pt1 = t1;
+        return true;
+      }
     }
     return false;
   };
 
+  // per-thread load/store geometry: chunk tid + k*256 of the super-tile
+  const int lrow = tid / G::kCPR, lcol = tid - lrow * G::kCPR;
+  const int st_off = lrow * PD::kStride + lcol * 16;
   u32x4 pre[kLoads];
   auto gload = [&]() {
-    const char* base = (const char*)a.D + (pd * a.Ld + pt * kTile) * (int64_t)G::kRowBytes;
-    const int64_t rows_left = a.Ld - pt * kTile;
+    const char* base = (const char*)a.D + ((int64_t)pd * a.Ld + (int64_t)pt * kTile) * G::kRowBytes;
+    const int rows = min(pt1 * kTile, (int)a.Ld) - pt * kTile;
+    const int nbytes = min(rows, kSTRows) * G::kRowBytes;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
-      const int idx = tid + k * kApThreads;
-      const int row = idx / G::kCPR;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      pre[k] = (idx < G::kTileChunks && row < rows_left) ? ld_global_16(base + idx * 16) : z;
+      // one descriptor per step keeps the per-lane offset constant and the
+      // range check (which covers the per-lane offset only) exact
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(base + k * kBytesPerLoad), 0, max(nbytes - k * kBytesPerLoad, 0), 0x00020000);
+      pre[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, 0, 0);
     }
   };
   auto lstore = [&](char* buf) {
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int idx = tid + k * kApThreads;
-      const int row = idx / G::kCPR, c = idx - row * G::kCPR;
-      if (idx < G::kTileChunks) st_lds_16(buf, lds_off<E, DIM>(row, c), pre[k]);
-    }
+    for (int k = 0; k < kLoads; ++k) st_lds_16(buf, st_off + k * kRowsPerLoad * PD::kStride, pre[k]);
   };
 
   int cur = 0;
@@ -194,35 +258,51 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   }
   __syncthreads();
 
-  for (int64_t u = u_begin; u < u_end; ++u) {
-    int64_t d, t0, t1;
-    unit_tiles(u, d, t0, t1);
-    const uint32_t* bits_d = a.bits ? a.bits + d * a.nwords : nullptr;
+  const int a_off = r * PD::kStride + h * 16;
+  f32x16 X[NB];
+  int cd = d_begin, cc = c_begin, cnt = doc_tiles(d_begin);
+  for (int k = 0; k < n_my; ++k) {
+    if (k > 0 && ++cc == nchunks) {
+      cc = 0;
+      ++cd;
+      cnt = doc_tiles(cd);
+    }
+    int t0, t1;
+    chunk_range(cnt, cc, t0, t1);
+    const uint32_t* bits_d = MASK ? a.bits + (int64_t)cd * a.nwords : nullptr;
     BlockState st[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) state_init(st[b], (int)t0);
+    for (int b = 0; b < NB; ++b) state_init(st[b], t0);
 
-    for (int64_t t = t0; t < t1; ++t) {
+    for (int t = t0; t < t1; t += kSub) {
+      // tile words are read before the prefetch is issued: loads retire in
+      // order, so a word read after it would also wait for the prefetch
+      uint32_t word0, word1;
+      if constexpr (MASK) {
+        word0 = __builtin_amdgcn_readfirstlane(bits_d[t]);
+        word1 = __builtin_amdgcn_readfirstlane(bits_d[min(t + 1, t1 - 1)]);
+      } else {
+        word0 = tile_word(nullptr, t, a.Ld);
+        word1 = tile_word(nullptr, t + 1, a.Ld);
+      }
+      const bool two = t + 1 < t1;
+      // inside the loop a tile exists, so the cursor is valid
       const bool nxt = advance();
-      if (nxt) gload();
+      gload();
       if (active) {
-        const uint32_t word = tile_word(bits_d, (int)t, a.Ld);
-        if (word != 0u) {
-          f32x16 acc[NB];
+        const char* buf = lds + cur * kSTBytes;
+        mfma_tile_pad<E, DIM, NB>(X, buf, bf, a_off);
+        if (word0 != kFull) tiles_mask<NB>(X, word0, h);
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-          const char* buf = lds + cur * G::kTileBytes;
+        for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t);
+        if (two) {
+          mfma_tile_pad<E, DIM, NB>(X, buf + PD::kTileBytes, bf, a_off);
+          if (word1 != kFull) tiles_mask<NB>(X, word1, h);
 #pragma unroll
-          for (int m = 0; m < G::kKSteps; ++m) {
-            const u32x4 av = ld_lds_16(buf, lds_off<E, DIM>(r, 2 * m + h));
-#pragma unroll
-            for (int b = 0; b < NB; ++b) mfma_chunk<E>(acc[b], av, bf[b][m]);
-          }
-#pragma unroll
-          for (int b = 0; b < NB; ++b) state_update(st[b], acc[b], word, (int)t, h);
+          for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t + 1);
         }
       }
-      if (nxt) lstore(lds + (cur ^ 1) * G::kTileBytes);
+      if (nxt) lstore(lds + (cur ^ 1) * kSTBytes);
       __syncthreads();
       cur ^= 1;
     }
@@ -236,28 +316,20 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     float Mv;
     int Jv;
     combine_halves<NB>(M, J, lane, Mv, Jv);
-    const int L = NB == 2 ? lane : (lane & 31);
-    const bool writer = NB == 2 || lane < 32;
     if (a.partial) {
-      const int64_t c = u - d * a.nchunks;
       const bool any = t1 > t0;
       if (writer) {
-        const int64_t idx = ((c * a.n_docs + d) * a.n_cg + gw) * SPW + L;
+        const int64_t idx = (((int64_t)cc * a.n_docs + cd) * a.n_cg + gw) * SPW + L;
         a.part_M[idx] = any ? Mv : -__builtin_inff();
         a.part_J[idx] = any ? Jv : -1;
       }
     } else {
       const bool empty = t1 == 0;   // single chunk: t1 is the doc's tile count
-      int64_t q, i;
-      const bool ok = slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, q, i);
-      const bool tok = ok && (!a.q_mask || a.q_mask[q * a.Lq + i]);
-      const float v = tok ? Mv : 0.0f;
-      const int seg_start = (int)((L / a.Lq) * a.Lq);
-      const float s = segmented_scan<SPW>(v, L, seg_start);
-      if (ok && writer) {
-        const int64_t pair = q * a.n_docs + d;
-        if (i == a.Lq - 1) a.scores[pair] = empty ? kEmptyDocScore : s;
-        if (a.argmax) a.argmax[pair * a.Lq + i] = (tok && !empty) ? Jv : -1;
+      const float s = segmented_scan<SPW>(slot_tok ? Mv : 0.0f, L, seg_start);
+      if (slot_ok && writer) {
+        const int64_t pair = slot_q * a.n_docs + cd;
+        if (seg_last) a.scores[pair] = empty ? kEmptyDocScore : s;
+        if (a.argmax) a.argmax[pair * a.Lq + slot_i] = (slot_tok && !empty) ? Jv : -1;
       }
     }
   }
@@ -272,7 +344,7 @@ constexpr int pr_waves() {
   return Geo<E, DIM>::kTileBytes * 4 <= 65536 ? 4 : (Geo<E, DIM>::kTileBytes * 2 <= 65536 ? 2 : 1);
 }
 
-template <Elem E, int DIM, int NB>
+template <Elem E, int DIM, int NB, bool MASK>
 __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
   using G = Geo<E, DIM>;
   constexpr int kPrWaves = pr_waves<E, DIM>();
@@ -306,23 +378,24 @@ __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
     load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
   }
 
-  const int64_t nt = a.ntiles ? (int64_t)a.ntiles[p] : a.ntiles_max;
+  const int64_t nt = MASK ? (int64_t)a.ntiles[p] : a.ntiles_max;
   const int64_t t0 = c * a.tpc;
   int64_t t1 = min(t0 + a.tpc, nt);
   if (t1 < t0) t1 = t0;
-  const uint32_t* bits_d = a.bits ? a.bits + p * a.nwords : nullptr;
+  const uint32_t* bits_d = MASK ? a.bits + p * a.nwords : nullptr;
   const char* docp = (const char*)a.D + p * a.Ld * (int64_t)G::kRowBytes;
 
+  // rows past the document repeat its last row (masked before any max)
   u32x4 pre[kLoads];
   auto gload = [&](int64_t t) {
     const char* base = docp + t * kTile * (int64_t)G::kRowBytes;
-    const int64_t rows_left = a.Ld - t * kTile;
+    const int rows_left = (int)min((int64_t)kTile, a.Ld - t * kTile);   // >= 1
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
       const int idx = lane + k * kWave;
-      const int row = idx / G::kCPR;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      pre[k] = row < rows_left ? ld_global_16(base + idx * 16) : z;
+      const int row = idx / G::kCPR, c = idx - row * G::kCPR;
+      const int rr = min(row, rows_left - 1);
+      pre[k] = ld_global_16(base + (rr * G::kCPR + c) * 16);
     }
   };
 
@@ -338,9 +411,12 @@ __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
       const int row = idx / G::kCPR, cc = idx - row * G::kCPR;
       st_lds_16(buf, lds_off<E, DIM>(row, cc), pre[k]);
     }
-    if (t + 1 < t1) gload(t + 1);
+    // The word is read before the next prefetch (loads retire in order) and
+    // the prefetch is unconditional (the last tile re-reads itself from L2),
+    // so the wait before the MFMAs covers only the word.
+    const uint32_t word = MASK ? bits_d[t] : tile_word(nullptr, (int)t, a.Ld);
+    gload(min(t + 1, t1 - 1));
     __asm__ volatile("" ::: "memory");
-    const uint32_t word = tile_word(bits_d, (int)t, a.Ld);
     if (word != 0u) {
       f32x16 acc[NB];
 #pragma unroll
@@ -432,20 +508,32 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <Elem E, int DIM, int NB>
-static hipError_t launch_main(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
+template <Elem E, int DIM, int NB, bool MASK>
+static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
   if (p.layout == kAllPairs) {
     const int64_t grid = 8 * p.gpx * p.n_sb;
-    hipLaunchKernelGGL((allpairs_fwd_kernel<E, DIM, NB>), dim3((unsigned)grid), dim3(kApThreads),
-                       2 * G::kTileBytes, s, a);
+    constexpr int lds = ap_lds_bytes<E, DIM>();
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&allpairs_fwd_kernel<E, DIM, NB, MASK>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((allpairs_fwd_kernel<E, DIM, NB, MASK>), dim3((unsigned)grid),
+                       dim3(kApThreads), lds, s, a);
   } else {
     constexpr int W = pr_waves<E, DIM>();
     const int64_t grid = cdiv(p.n_units, W);
-    hipLaunchKernelGGL((pairs_fwd_kernel<E, DIM, NB>), dim3((unsigned)grid), dim3(W * kWave),
-                       W * G::kTileBytes, s, a);
+    hipLaunchKernelGGL((pairs_fwd_kernel<E, DIM, NB, MASK>), dim3((unsigned)grid),
+                       dim3(W * kWave), W * G::kTileBytes, s, a);
   }
   return hipGetLastError();
+}
+
+template <Elem E, int DIM, int NB>
+static hipError_t launch_main(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
+  return a.bits ? launch_main_m<E, DIM, NB, true>(p, a, s) : launch_main_m<E, DIM, NB, false>(p, a, s);
 }
 
 template <Elem E>

@@ -44,7 +44,8 @@ struct BwdPlan {
   bool recompute = false;
   int64_t H = 0;            // hits per document (all-pairs Nq*Lq; pairs Lq)
   int key_bits = 1;
-  size_t off_argmax = 0, off_scores = 0, off_sorted = 0, off_roff = 0, off_fwd = 0, total = 0;
+  size_t off_argmax = 0, off_scores = 0, off_sorted = 0, off_sorted_g = 0, off_roff = 0, off_fwd = 0,
+         total = 0;
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -65,6 +66,8 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
   p.elem = elem;
   p.dim = (int)dim;
   p.NB = blocks_per_wave(elem, dim);
+  // a pair has one query: one 32-column block suffices when Lq <= 32
+  if (layout != kAllPairs && Lq <= 32) p.NB = 1;
   p.SPW = 32 * p.NB;
   p.Nq = nq_or_b;
   p.Lq = Lq;
@@ -104,7 +107,7 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
       p.qpw = 0;
       p.n_cg = cdiv(p.Nq * Lq, p.SPW);
     }
-    p.NW = 8;
+    p.NW = 4;   // waves per workgroup of the all-pairs kernel
     p.n_sb = cdiv(p.n_cg, p.NW);
     // Long documents are cut into chunks of 32 tiles (1024 rows) so that
     // work units stay short and the chip fills; chunk maxima merge exactly.
@@ -171,6 +174,8 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
   }
   if (Lq > 0 && Ld > 0) {
     b.off_sorted = off;
+    off = align256(off + (size_t)f.n_docs * b.H * 4);
+    b.off_sorted_g = off;
     off = align256(off + (size_t)f.n_docs * b.H * 4);
     b.off_roff = off;
     off = align256(off + (size_t)f.n_docs * (Ld + 1) * 4);
