@@ -416,6 +416,23 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
     return line
 
 
+def copy_calibration(mib: int, reps: int):
+    """Plain device-to-device copies of `mib` MiB: under rocprofv3 the copy
+    kernel's FETCH_SIZE / WRITE_SIZE per dispatch, divided by the known byte
+    count, is the scale factor applied to the MaxSim kernels' counters."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +440,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="inbatch-text")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of a workload, run plain device copies of MIB MiB "
+                         "(reference kernel for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this operator build has no multi-GPU path "
@@ -433,6 +453,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
     names = (["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"]
              if args.workload == "all" else [args.workload])
     for i, name in enumerate(names):
