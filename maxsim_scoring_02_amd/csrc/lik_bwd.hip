@@ -6,13 +6,24 @@
 //   grad_Q[q,i,:] = sum over the pairs p of query q of g[p] * D[doc(p), a(p,i), :]
 //   grad_D[e,j,:] = sum over (p, i) with doc(p) = e and a(p,i) = j of g[p] * Q[q(p), i, :]
 // Masked query tokens and empty documents carry argmax -1 and contribute
-// nothing.
+// nothing.  No floating-point atomics anywhere: every output row has one
+// owner that adds its terms in an order fixed by the inputs alone.
 //
-//   gradq_kernel       gather: one lane group per (query token, 16-byte chunk)
-//   gradd_sort_kernel  per document, a stable counting sort of its hits by
-//                      row j (integer LDS histogram, ballot ranks), so that
-//   gradd_rows_kernel  can give every row of grad_D one owner that sums its
-//                      hits in a fixed order: deterministic, no float atomics.
+//   grad_Q
+//     gradq_xcd_kernel     all-pairs with many documents: the documents are cut
+//                          into 8 slices, one per XCD, so each XCD gathers from an
+//                          L2-resident slice of D; gradq_reduce_kernel adds the
+//                          slice partials in slice order
+//     gradq_kernel         few documents per query (pairwise, kd, small Nd)
+//   grad_D
+//     gradd_fused_kernel   all-pairs: per document, a stable counting sort of
+//                          its hits by row in LDS, then lane groups sum equal
+//                          shares of the sorted hits; rows cut by a share
+//                          boundary are finished by the group where they start
+//     gradd_pairs_kernel   pairwise / kd: a wave per document streams the
+//                          (mostly zero) rows and sums the few hit rows inline
+//     gradd_sort_*_kernel + gradd_rows_group_kernel
+//                          general fallback through the workspace
 #include <hip/hip_runtime.h>
 
 #include "lik_device.h"
@@ -34,8 +45,13 @@ struct BwdArgs {
   int32_t* sorted;   // [n_docs][H] Q-row index of each hit, ordered by doc row, then hit id
   float* sorted_g;   // [n_docs][H] upstream gradient g[pair] of each sorted hit
   int32_t* roff;     // [n_docs][Ld + 1] row offsets into `sorted`
+  float* gq_part;    // [gq_slices][Nq * Lq][dim] grad_Q partials per document slice
   int layout;
   int key_bits;
+  int gq_slices;
+  int fz_sw, fz_split;                      // fused grad_D: sorting waves, workgroups per doc
+  int fz_off_start, fz_off_cnt, fz_off_sorted, fz_off_gl, fz_off_union, fz_off_masks;  // LDS layout
+  uint64_t lq_magic;                        // ceil(2^32 / Lq): h / Lq for h < 2^16
   int64_t Nq, Lq, n_docs, Ld, K, H;
 };
 
@@ -102,56 +118,64 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// grad_Q, sliced: one workgroup per (query, token); its threads are CPR
-// chunk lanes x NS document slices.  Every thread gathers its slice's rows
-// with all loads independent (one latency round trip for the indices, one
-// for the rows), and the NS slice partials of each chunk are added in slice
-// order through LDS: deterministic, and tens of thousands of rows in flight.
+// grad_Q, all-pairs, XCD-sliced.  Workgroups are dispatched round-robin over
+// the 8 XCDs, so workgroup b runs on XCD b % 8; it gathers only from document
+// slice b % gq_slices, and with 8 slices each XCD reads one eighth of D,
+// which stays in that XCD's L2.  Thread = (query token, 16-byte chunk); all
+// its row loads of a round are independent.  Partials go to gq_part.
 // ---------------------------------------------------------------------------
 template <Elem E, int DIM>
-__global__ __launch_bounds__(256) void gradq_sliced_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void gradq_xcd_kernel(BwdArgs a) {
   using G = Geo<E, DIM>;
   constexpr int EPC = ElemInfo<E>::kPerChunk;
   constexpr int CPR = G::kCPR;
-  constexpr int NS = 256 / CPR;            // document slices
-  constexpr int U = 16;                    // rows per round
-  __shared__ float part[NS][CPR * EPC];
-  const int tid = threadIdx.x;
-  const int c = tid % CPR, sl = tid / CPR;
-  const int64_t qi = blockIdx.x;           // q * Lq + i
+  constexpr int TPB = 256 / CPR;           // query tokens per workgroup
+  constexpr int U = CPR < 16 ? CPR : 16;   // documents per round (one index load per lane)
+  const int ns = a.gq_slices;
+  const int sl = (int)(blockIdx.x % ns);
+  const int64_t tb = blockIdx.x / ns;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int t = tid / CPR, c = tid - t * CPR;
+  const int base_lane = lane - c;          // lane of chunk 0 of this token
+  const int64_t n_tok = a.Nq * a.Lq;
+  const int64_t qi = min(tb * TPB + t, n_tok - 1);  // a clamped token computes, never stores
+  const bool tok_ok = tb * TPB + t < n_tok;
   const int64_t q = qi / a.Lq, i = qi - q * a.Lq;
-  const bool ap = a.layout == kAllPairs;
-  const int64_t K = ap ? a.n_docs : a.K;
-  const int64_t per = (K + NS - 1) / NS;
-  const int64_t k_lo = min(sl * per, K), k_hi = min(k_lo + per, K);
+  const int64_t Nd = a.n_docs;
+  const int64_t d0 = Nd * sl / ns, d1 = Nd * (sl + 1) / ns;
   const char* Db = (const char*)a.D;
   float acc[EPC];
 #pragma unroll
   for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-  for (int64_t k0 = k_lo; k0 < k_hi; k0 += U) {
-    int jj[U];
-    float gg[U];
-    int64_t dd[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = k0 + u;
-      jj[u] = -1;
-      gg[u] = 0.0f;
-      dd[u] = 0;
-      if (k < k_hi) {
-        const int64_t p = q * K + k;
-        dd[u] = ap ? k : p;
-        jj[u] = a.argmax[p * a.Lq + i];
-        gg[u] = a.g[p];
-      }
+  // round r: lane c of a token loads the index and weight of document
+  // k0 + c; every lane of the token then takes all U of them by lane swaps
+  auto fetch_idx = [&](int64_t k0, int& j, float& w) {
+    const int64_t d = k0 + c;
+    j = -1;
+    w = 0.0f;
+    if (c < U && d < d1) {
+      const int64_t p = q * Nd + d;
+      j = a.argmax[p * a.Lq + i];
+      w = a.g[p];
     }
+  };
+  int jn;
+  float wn;
+  fetch_idx(d0, jn, wn);
+  for (int64_t k0 = d0; k0 < d1; k0 += U) {
+    const int jc = jn;
+    const float wc = wn;
+    fetch_idx(k0 + U, jn, wn);             // next round's indices in flight
     u32x4 ch[U];
+    float gg[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = jj[u] >= 0 && jj[u] < a.Ld;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      ch[u] = ok ? ld_global_16(Db + (dd[u] * a.Ld + jj[u]) * (int64_t)G::kRowBytes + c * 16) : z;
-      if (!ok) gg[u] = 0.0f;
+      const int j = __shfl(jc, base_lane + u);
+      const float w = __shfl(wc, base_lane + u);
+      const bool ok = j >= 0 && j < a.Ld;
+      const int64_t d = ok ? k0 + u : 0;
+      ch[u] = ld_global_16(Db + (d * a.Ld + (ok ? j : 0)) * (int64_t)G::kRowBytes + c * 16);
+      gg[u] = ok ? w : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -161,22 +185,27 @@ __global__ __launch_bounds__(256) void gradq_sliced_kernel(BwdArgs a) {
       for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[u], f[k], acc[k]);
     }
   }
+  if (!tok_ok) return;
+  float* out = a.gq_part + ((int64_t)sl * n_tok + qi) * DIM + c * EPC;
 #pragma unroll
-  for (int k = 0; k < EPC; ++k) part[sl][c * EPC + k] = acc[k];
-  __syncthreads();
-  // thread t < CPR*EPC/4 sums one float4 of the row over the slices in order
-  constexpr int NV = CPR * EPC / 4;
-  if (tid < NV) {
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int x = 0; x < NS; ++x) {
-      const float4 v = *reinterpret_cast<const float4*>(&part[x][tid * 4]);
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
-    }
-    *reinterpret_cast<float4*>(a.gQ + qi * DIM + tid * 4) = sum;
+  for (int k = 0; k < EPC; k += 4)
+    *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+}
+
+// grad_Q = sum of the slice partials, added in slice order.
+__global__ __launch_bounds__(256) void gradq_reduce_kernel(const float4* __restrict__ part, int ns,
+                                                           int64_t n4, float4* __restrict__ gQ) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= n4) return;
+  float4 s = part[k];
+  for (int x = 1; x < ns; ++x) {
+    const float4 v = part[(int64_t)x * n4 + k];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
   }
+  gQ[k] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -283,69 +312,6 @@ __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// grad_D, step 2: one lane group per row sums its hits in sorted order
-// ---------------------------------------------------------------------------
-template <Elem E, int DIM>
-__global__ __launch_bounds__(256) void gradd_rows_kernel(BwdArgs a) {
-  using G = Geo<E, DIM>;
-  constexpr int EPC = ElemInfo<E>::kPerChunk;
-  constexpr int CPR = G::kCPR;
-  constexpr int RPB = 256 / CPR;
-  const int tid = threadIdx.x;
-  const int rk = tid / CPR, c = tid - rk * CPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + rk;
-  if (row >= a.n_docs * a.Ld) return;
-  const int64_t e = row / a.Ld;
-  const int64_t j = row - e * a.Ld;
-  const int32_t* roff = a.roff + e * (a.Ld + 1);
-  const int s = max(0, min(roff[j], (int)a.H));
-  const int t = max(s, min(roff[j + 1], (int)a.H));
-  const int32_t* lst = a.sorted + e * a.H;
-  const bool ap = a.layout == kAllPairs;
-  const char* Qb = (const char*)a.Q;
-  float acc[EPC];
-#pragma unroll
-  for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-  constexpr int U = 4;
-  for (int k0 = s; k0 < t; k0 += U) {
-    float gg[U];
-    int64_t qrow[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      gg[u] = 0.0f;
-      qrow[u] = 0;
-      if (k0 + u < t) {
-        const int64_t h = min(max((int64_t)lst[k0 + u], (int64_t)0), a.H - 1);
-        int64_t p;
-        if (ap) {
-          const int64_t q = h / a.Lq;
-          p = q * a.n_docs + e;
-          qrow[u] = h;
-        } else {
-          p = e;
-          qrow[u] = (e / a.K) * a.Lq + h;
-        }
-        gg[u] = a.g[p];
-      }
-    }
-    u32x4 ch[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) ch[u] = ld_global_16(Qb + qrow[u] * (int64_t)G::kRowBytes + c * 16);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f[EPC];
-      chunk_to_float<E>(ch[u], f);
-#pragma unroll
-      for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[u], f[k], acc[k]);
-    }
-  }
-  float* out = a.gD + row * DIM + c * EPC;
-#pragma unroll
-  for (int k = 0; k < EPC; k += 4)
-    *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
-}
-
-// ---------------------------------------------------------------------------
 // grad_D, step 1 (parallel form): each of the 4 waves owns a contiguous
 // quarter of the document's hits and its own row histogram, so the stable
 // placement needs no cross-wave turns: a hit's slot is the row's start, plus
@@ -440,85 +406,6 @@ __global__ __launch_bounds__(256) void gradd_sort_waves_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// grad_D, step 2 (wave per row): the wave's lanes form 64/CPR entry groups;
-// group k takes the row's entries k, k + groups, ... (in sorted order) and the
-// group partials are added by a fixed xor tree, so the sum order depends only
-// on the row's entry list: deterministic, and long rows are spread over the
-// whole wave.  Each wave walks `rpw` consecutive rows.
-// ---------------------------------------------------------------------------
-template <Elem E, int DIM>
-__global__ __launch_bounds__(256) void gradd_rows_wave_kernel(BwdArgs a, int rpw) {
-  using G = Geo<E, DIM>;
-  constexpr int EPC = ElemInfo<E>::kPerChunk;
-  constexpr int CPR = G::kCPR;
-  constexpr int EG = CPR >= 64 ? 1 : 64 / CPR;    // entry groups per wave
-  constexpr int U = 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = CPR >= 64 ? 0 : lane / CPR, c = CPR >= 64 ? lane : lane - grp * CPR;
-  const int64_t n_rows = a.n_docs * a.Ld;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * rpw;
-  const bool ap = a.layout == kAllPairs;
-  const char* Qb = (const char*)a.Q;
-  for (int rr = 0; rr < rpw; ++rr) {
-    const int64_t row = row0 + rr;
-    if (row >= n_rows) break;
-    const int64_t e = row / a.Ld;
-    const int64_t j = row - e * a.Ld;
-    const int32_t* roff = a.roff + e * (a.Ld + 1);
-    const int s = max(0, min(roff[j], (int)a.H));
-    const int t = max(s, min(roff[j + 1], (int)a.H));
-    const int32_t* lst = a.sorted + e * a.H;
-    float acc[EPC];
-#pragma unroll
-    for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-    for (int k0 = s; k0 < t; k0 += EG * U) {
-      float gg[U];
-      int64_t qrow[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + u * EG + grp;
-        gg[u] = 0.0f;
-        qrow[u] = 0;
-        if (k < t) {
-          const int64_t h = min(max((int64_t)lst[k], (int64_t)0), a.H - 1);
-          int64_t p;
-          if (ap) {
-            const int64_t q = h / a.Lq;
-            p = q * a.n_docs + e;
-            qrow[u] = h;
-          } else {
-            p = e;
-            qrow[u] = (e / a.K) * a.Lq + h;
-          }
-          gg[u] = a.g[p];
-        }
-      }
-      u32x4 ch[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        ch[u] = ld_global_16(Qb + qrow[u] * (int64_t)G::kRowBytes + c * 16);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float f[EPC];
-        chunk_to_float<E>(ch[u], f);
-#pragma unroll
-        for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[u], f[k], acc[k]);
-      }
-    }
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int k = 0; k < EPC; ++k) acc[k] += __shfl_xor(acc[k], off);
-    if (grp == 0) {
-      float* out = a.gD + row * DIM + c * EPC;
-#pragma unroll
-      for (int k = 0; k < EPC; k += 4)
-        *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // grad_D, step 2 (lane group per row): a group of CPR lanes (one 16-byte
 // chunk of the row each) owns `rpg` consecutive rows.  The rows' offsets come
 // in one load; a row's (Q row, g) pairs come 16 at a time, the next 16
@@ -596,6 +483,418 @@ __global__ __launch_bounds__(256) void gradd_rows_group_kernel(BwdArgs a, int rp
       *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
   }
 }
+// ---------------------------------------------------------------------------
+// grad_D, all-pairs, fused: workgroup (document e, split s) of kFzThreads.
+//
+//  1. keys: the row a(q,e,i) of every hit h = q*Lq + i (0xffff for none), and
+//     (the row histograms of each sorting wave come with the ranks of step 3);
+//  2. row starts (exclusive scan) and per-wave cursors; the document's valid
+//     hits are cut into fz_split equal shares at row boundaries, and this
+//     workgroup owns the rows [c0, c1) of share s;
+//  3. stable placement: sorting wave w walks its contiguous hit range in
+//     64-hit chunks; a hit's slot is its row's cursor plus its rank among the
+//     chunk's hits of the same row, so the sorted list is ordered by row,
+//     then by h;
+//  4. the sorted hits of [c0, c1) are cut into NG equal ranges, one per lane
+//     group of CPR lanes (16 bytes of the row each).  A group adds g * Q[h]
+//     over its range in sorted order and writes each row it holds whole; a row
+//     cut by a range boundary leaves a partial in LDS, and after a barrier the
+//     group where that row starts adds the later groups' partials in group
+//     order.  Rows without hits are written as zeros.
+// The sums depend only on the sorted list, so results are bitwise stable.
+// ---------------------------------------------------------------------------
+constexpr int kFzWaves = kFzThreads / kWave;
+constexpr int kFzMaxChunks = kFzMaxHitsPerWave / 64;   // 64-hit chunks per sorting wave
+
+// h / Lq for 0 <= h < 2^16 and 1 <= Lq <= 2^16, with magic = ceil(2^32 / Lq):
+// the rounding error of the product is below 2^-16 <= 1/Lq, so the floor is exact.
+__device__ __forceinline__ int div_lq(int h, uint64_t magic) {
+  return (int)(((uint64_t)(uint32_t)h * magic) >> 32);
+}
+
+template <Elem E, int DIM>
+__global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4))) void gradd_fused_kernel(BwdArgs a) {
+  using G = Geo<E, DIM>;
+  constexpr int EPC = ElemInfo<E>::kPerChunk;
+  constexpr int CPR = G::kCPR;
+  constexpr int NG = kFzThreads / CPR;     // lane groups
+  constexpr int B = 6;                     // hits per batch
+  constexpr int F4 = DIM / 4;              // float4 per gradient row
+  extern __shared__ __attribute__((aligned(16))) char fz_smem[];
+  char* smem = fz_smem;
+  int32_t* start = reinterpret_cast<int32_t*>(smem + a.fz_off_start);     // [Ld + 1]
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + a.fz_off_cnt);         // [SW][Ld]
+  uint32_t* sorted = reinterpret_cast<uint32_t*>(smem + a.fz_off_sorted); // [H]: row << 16 | h
+  float* gl = reinterpret_cast<float*>(smem + a.fz_off_gl);               // [Nq]
+  uint16_t* keys = reinterpret_cast<uint16_t*>(smem + a.fz_off_union);    // [H] (steps 1-3)
+  uint64_t* masks = reinterpret_cast<uint64_t*>(smem + a.fz_off_masks);   // [SW][Ld] (step 3a)
+  float* part = reinterpret_cast<float*>(smem + a.fz_off_union);          // [NG][2][DIM] (step 4)
+  __shared__ int wtot[kFzWaves];
+  __shared__ int cut[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = a.fz_split;
+  const int64_t e = blockIdx.x / split;
+  const int s = (int)(blockIdx.x - e * split);
+  const int Ld = (int)a.Ld, H = (int)a.H, Lq = (int)a.Lq, Nq = (int)a.Nq;
+  const int SW = a.fz_sw;
+  const int Hw = ((H + SW * 64 - 1) / (SW * 64)) * 64;   // hits per sorting wave
+  const int64_t Nd = a.n_docs;
+
+  // 0. clear the histograms and match masks; this document's upstream grads
+  for (int k = tid; k < SW * Ld; k += kFzThreads) {
+    cnt[k] = 0;
+    masks[k] = 0ull;
+  }
+  for (int q = tid; q < Nq; q += kFzThreads) gl[q] = a.g[(int64_t)q * Nd + e];
+
+  // 1. keys: the row of every hit (16 independent argmax loads per thread)
+  constexpr int UL = 16;
+  for (int hb = tid; hb < H; hb += kFzThreads * UL) {
+    int jj[UL];
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      const int h = hb + u * kFzThreads;
+      jj[u] = -1;
+      if (h < H) {
+        const int q = div_lq(h, a.lq_magic);
+        const int i = h - q * Lq;
+        jj[u] = a.argmax[((int64_t)q * Nd + e) * Lq + i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      const int h = hb + u * kFzThreads;
+      if (h < H) keys[h] = (jj[u] >= 0 && jj[u] < Ld) ? (uint16_t)jj[u] : (uint16_t)0xffff;
+    }
+  }
+  __syncthreads();
+
+  // 3a. sorting wave w takes hits [w*Hw, (w+1)*Hw) in chunks of 64.  The lanes
+  // of a chunk holding the same row find each other through an LDS mask that
+  // each ORs its lane bit into (OR is order-free, so the mask is exact); a
+  // hit's rank is the number of such lanes below it.  The last of them adds
+  // the chunk's count to the wave's row histogram.
+  const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  // per chunk: row (16 bits, 0xffff none) | rank << 16 | count << 23
+  int rc[kFzMaxChunks];
+  const int h0 = min(wave * Hw, H), h1 = min(h0 + Hw, H);
+  if (wave < SW) {
+    int* hist = cnt + wave * Ld;
+    unsigned long long* msk = reinterpret_cast<unsigned long long*>(masks + wave * Ld);
+    constexpr int CG = 4;                        // chunks whose LDS traffic is in flight together
+#pragma unroll
+    for (int g0 = 0; g0 < kFzMaxChunks; g0 += CG) {
+      if (h0 + g0 * 64 >= h1) break;
+      int jj[CG];
+      uint64_t same[CG];
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const int h = h0 + (g0 + u) * 64 + lane;
+        jj[u] = h < h1 ? (int)keys[h] : 0xffff;
+      }
+      // OR, read back and clear, chunk after chunk: LDS runs a wave's
+      // operations in order, so no wait is needed between them
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const bool v = jj[u] != 0xffff;
+        if (v) atomicOr(&msk[jj[u]], 1ull << lane);
+        same[u] = v ? (uint64_t)msk[jj[u]] : 0ull;
+        if (v) msk[jj[u]] = 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const bool v = jj[u] != 0xffff;
+        const int rank = __popcll(same[u] & below);
+        const int count = __popcll(same[u]);
+        rc[g0 + u] = jj[u] | (rank << 16) | (count << 23);
+        if (v && rank == count - 1) atomicAdd(&hist[jj[u]], count);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. row starts and per-wave cursors (each thread scans a segment of rows)
+  {
+    const int seg = (Ld + kFzThreads - 1) / kFzThreads;
+    const int lo = min(tid * seg, Ld), hi = min(lo + seg, Ld);
+    int local = 0;
+    for (int j = lo; j < hi; ++j)
+      for (int w = 0; w < SW; ++w) local += cnt[w * Ld + j];
+    int incl = local;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const int t = __shfl_up(incl, k);
+      if (lane >= k) incl += t;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int base = incl - local;
+    for (int w = 0; w < wave; ++w) base += wtot[w];
+    for (int j = lo; j < hi; ++j) {
+      start[j] = base;
+      for (int w = 0; w < SW; ++w) {
+        const int c = cnt[w * Ld + j];
+        cnt[w * Ld + j] = base;
+        base += c;
+      }
+    }
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < kFzWaves; ++w) tot += wtot[w];
+      start[Ld] = tot;
+    }
+  }
+  __syncthreads();
+  if (tid < 2) {
+    // share boundary k: the first row whose hits reach past position Hv*k/split
+    const int k = s + tid;
+    const int Hv = start[Ld];
+    int r = (k == 0) ? 0 : Ld;
+    if (k > 0 && k < split) {
+      const int P = (int)((int64_t)Hv * k / split);
+      int lo = 0, hi = Ld;                       // smallest r with start[r+1] > P
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (start[mid + 1] > P) hi = mid; else lo = mid + 1;
+      }
+      r = lo;
+    }
+    cut[tid] = r;
+  }
+  __syncthreads();
+  const int c0 = cut[0], c1 = cut[1];
+
+  // 3b. placement in chunk order: slot = the wave's cursor of the row + rank;
+  // the sorted list is ordered by row, then by h.  Only rows in [c0, c1).
+  if (wave < SW) {
+    int* cur = cnt + wave * Ld;
+#pragma unroll
+    for (int ch = 0; ch < kFzMaxChunks; ++ch) {
+      if (h0 + ch * 64 >= h1) break;
+      const int h = h0 + ch * 64 + lane;
+      const int j = rc[ch] & 0xffff;
+      const bool v = j != 0xffff;
+      const int rank = (rc[ch] >> 16) & 0x7f, count = rc[ch] >> 23;
+      const int pos = v ? cur[j] : 0;
+      __asm__ volatile("" ::: "memory");
+      if (v && j >= c0 && j < c1) sorted[pos + rank] = ((uint32_t)j << 16) | (uint32_t)h;
+      if (v && rank == count - 1) cur[j] = pos + count;
+    }
+  }
+  __syncthreads();
+
+  // 4. row sums over equal shares of the sorted hits.  Inside the hit loop a
+  // finished row is either whole (stored to grad_D) or the range's first row
+  // begun in an earlier range (kept in registers); partials reach LDS only
+  // after the loop, so the loop holds no LDS stores and one kind of global
+  // store, and the next batch's rows are in flight while a batch is summed.
+  const int H0 = start[c0], H1 = start[c1];
+  const int grp = tid / CPR, c = tid - grp * CPR;
+  auto range_lo = [&](int k) { return H0 + (int)((int64_t)(H1 - H0) * k / NG); };
+  const int lo = range_lo(grp), hi = range_lo(grp + 1);
+  float* __restrict__ gD_doc = a.gD + e * (int64_t)Ld * DIM;
+  const char* Qb = (const char*)a.Q;
+  float acc[EPC], head[EPC];
+#pragma unroll
+  for (int k = 0; k < EPC; ++k) acc[k] = head[k] = 0.0f;
+  int cur_row = lo < hi ? (int)(sorted[lo] >> 16) : -1;
+  bool in_head = lo < hi && start[cur_row] < lo;   // first row began in an earlier range
+  bool have_head = false;
+  auto fetch = [&](int p0, uint32_t (&en)[B], u32x4 (&cq)[B], float (&gq)[B]) {
+#pragma unroll
+    for (int m = 0; m < B; ++m) en[m] = (p0 + m < hi) ? sorted[p0 + m] : 0u;
+#pragma unroll
+    for (int m = 0; m < B; ++m) {
+      const int h = (int)(en[m] & 0xffffu);    // 0 past the range: a valid row, weight 0
+      cq[m] = ld_global_16(Qb + (int64_t)h * G::kRowBytes + c * 16);
+      gq[m] = (p0 + m < hi) ? gl[div_lq(h, a.lq_magic)] : 0.0f;
+    }
+  };
+  auto consume = [&](int p0, const uint32_t (&en)[B], const u32x4 (&cq)[B], const float (&gq)[B]) {
+#pragma unroll
+    for (int m = 0; m < B; ++m) {
+      const int row = (p0 + m < hi) ? (int)(en[m] >> 16) : cur_row;
+      if (row != cur_row) {
+        if (in_head) {
+#pragma unroll
+          for (int k = 0; k < EPC; ++k) head[k] = acc[k];
+          have_head = true;
+          in_head = false;
+        } else {
+          float* out = gD_doc + (int64_t)cur_row * DIM + c * EPC;
+#pragma unroll
+          for (int k = 0; k < EPC; k += 4)
+            *reinterpret_cast<float4*>(out + k) =
+                make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+        }
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
+        cur_row = row;
+      }
+      float f[EPC];
+      chunk_to_float<E>(cq[m], f);
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gq[m], f[k], acc[k]);
+    }
+  };
+  // two batches per step: the second is in flight while the first is summed
+  // (no loads are carried across steps, so none is waited for early)
+  for (int p0 = lo; p0 < hi; p0 += 2 * B) {
+    uint32_t ea[B], eb[B];
+    u32x4 ca[B], cb[B];
+    float ga[B], gb[B];
+    fetch(p0, ea, ca, ga);
+    fetch(p0 + B, eb, cb, gb);
+    consume(p0, ea, ca, ga);
+    consume(p0 + B, eb, cb, gb);
+  }
+  // the range's last row: whole, a tail (continues in later ranges), or the
+  // head itself (the range lies inside one row)
+  int tail_row = -1;
+  if (cur_row >= 0) {
+    if (in_head) {
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) head[k] = acc[k];
+      have_head = true;
+    } else if (start[cur_row + 1] > hi) {
+      tail_row = cur_row;
+      float* out = part + (grp * 2 + 1) * DIM + c * EPC;
+#pragma unroll
+      for (int k = 0; k < EPC; k += 4)
+        *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+    } else {
+      float* out = gD_doc + (int64_t)cur_row * DIM + c * EPC;
+#pragma unroll
+      for (int k = 0; k < EPC; k += 4)
+        *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+    }
+  }
+  if (have_head) {
+    float* out = part + (grp * 2) * DIM + c * EPC;
+#pragma unroll
+    for (int k = 0; k < EPC; k += 4)
+      *reinterpret_cast<float4*>(out + k) = make_float4(head[k], head[k + 1], head[k + 2], head[k + 3]);
+  }
+  __syncthreads();
+
+  // rows cut by range boundaries: the group where the row starts finishes it
+  if (tail_row >= 0) {
+    const float* own = part + (grp * 2 + 1) * DIM + c * EPC;
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) acc[k] = own[k];
+    const int rt = start[tail_row + 1];
+    for (int k2 = grp + 1; k2 < NG; ++k2) {
+      const int lo2 = range_lo(k2), hi2 = range_lo(k2 + 1);
+      if (lo2 >= rt) break;
+      if (lo2 < hi2) {
+        const float* pp = part + (k2 * 2) * DIM + c * EPC;
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) acc[k] += pp[k];
+      }
+    }
+    float* out = gD_doc + (int64_t)tail_row * DIM + c * EPC;
+#pragma unroll
+    for (int k = 0; k < EPC; k += 4)
+      *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+  }
+  // rows of [c0, c1) without hits
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = tid; k < (c1 - c0) * F4; k += kFzThreads) {
+    const int row = c0 + k / F4, f = k - (k / F4) * F4;
+    if (start[row] == start[row + 1])
+      *reinterpret_cast<float4*>(gD_doc + (int64_t)row * DIM + 4 * f) = z;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grad_D, pairwise / kd: one wave per document.  A document has only Lq hits
+// (one per query token), so its gradient is Ld rows of which at most Lq are
+// non-zero: the wave streams the rows in order with non-temporal stores and,
+// for a row some hit points at, adds g * Q[h] over those hits in increasing
+// h (their lanes, found by ballot) before storing it.
+// ---------------------------------------------------------------------------
+
+template <Elem E>
+__device__ __forceinline__ void load4_as_float(const char* p, float (&f)[4]);
+template <> __device__ __forceinline__ void load4_as_float<Elem::BF16>(const char* p, float (&f)[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  f[0] = __uint_as_float(w.x << 16);
+  f[1] = __uint_as_float(w.x & 0xffff0000u);
+  f[2] = __uint_as_float(w.y << 16);
+  f[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void load4_as_float<Elem::F16>(const char* p, float (&f)[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  f[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xffffu));
+  f[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16));
+  f[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y & 0xffffu));
+  f[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y >> 16));
+}
+template <> __device__ __forceinline__ void load4_as_float<Elem::F32>(const char* p, float (&f)[4]) {
+  const float4 w = *reinterpret_cast<const float4*>(p);
+  f[0] = w.x;
+  f[1] = w.y;
+  f[2] = w.z;
+  f[3] = w.w;
+}
+
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
+  constexpr int F4 = DIM / 4;                 // float4 per gradient row
+  constexpr int RPI = F4 >= 64 ? 1 : 64 / F4; // rows per wave store
+  constexpr int NH = kPairsMaxLq / 64;        // hit registers per lane
+  constexpr int ES = ElemInfo<E>::kBytes;
+  static_assert(F4 <= 64, "one gradient row per wave store at most");
+  const int lane = threadIdx.x & 63;
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= a.n_docs) return;
+  const int Lq = (int)a.Lq, Ld = (int)a.Ld;
+  const int nh = (Lq + 63) / 64;
+  const float g = a.g[e];
+  const int64_t qbase = (e / a.K) * a.Lq;     // first Q row of this document's query
+  int key[NH];
+#pragma unroll
+  for (int k = 0; k < NH; ++k) {
+    const int h = 64 * k + lane;
+    int j = -1;
+    if (k < nh && h < Lq) j = a.argmax[e * a.Lq + h];
+    key[k] = (j >= 0 && j < Ld) ? j : -1;
+  }
+  const int sub = lane / F4, f = lane - (lane / F4) * F4;
+  float* out = a.gD + e * (int64_t)Ld * DIM;
+  const char* Qb = (const char*)a.Q;
+  for (int r0 = 0; r0 < Ld; r0 += RPI) {
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < NH; ++k) any |= (k < nh) && key[k] >= r0 && key[k] < r0 + RPI;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (__ballot(any) != 0ull) {
+      for (int rr = 0; rr < RPI; ++rr) {
+#pragma unroll
+        for (int k = 0; k < NH; ++k) {
+          if (k >= nh) break;
+          uint64_t m = __ballot(key[k] == r0 + rr);
+          while (m != 0ull) {
+            const int b = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            if (sub == rr) {
+              float x[4];
+              load4_as_float<E>(Qb + (qbase + 64 * k + b) * (int64_t)(DIM * ES) + 4 * f * ES, x);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(g, x[t], v[t]);
+            }
+          }
+        }
+      }
+    }
+    const int row = r0 + sub;
+    if (sub < RPI && row < Ld) {
+      const f32x4 w = {v[0], v[1], v[2], v[3]};
+      __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f));
+    }
+  }
+}
 
 __global__ void zero_kernel(float4* p, int64_t n4) {
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -612,55 +911,85 @@ static hipError_t zero_fill(float* p, int64_t n, hipStream_t s) {
 }
 
 template <Elem E, int DIM>
-static hipError_t launch_grads(const BwdArgs& a, bool want_q, bool want_d, hipStream_t s) {
+static hipError_t launch_gradq(const BwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
   constexpr int CPR = G::kCPR;
-  if (want_q) {
-    const int64_t K = a.layout == kAllPairs ? a.n_docs : a.K;
-    if (K >= 64) {
-      // many documents per query: split each (query, token) over slices
-      hipLaunchKernelGGL((gradq_sliced_kernel<E, DIM>), dim3((unsigned)(a.Nq * a.Lq)), dim3(256), 0,
-                         s, a);
-    } else {
-      const int64_t tpb = 256 / CPR;
-      hipLaunchKernelGGL((gradq_kernel<E, DIM>), dim3((unsigned)a.Nq, (unsigned)cdiv(a.Lq, tpb)),
-                         dim3(256), 0, s, a);
-    }
+  constexpr int TPB = 256 / CPR;
+  if (a.gq_slices > 1) {
+    const int64_t n_tok = a.Nq * a.Lq;
+    hipLaunchKernelGGL((gradq_xcd_kernel<E, DIM>), dim3((unsigned)(a.gq_slices * cdiv(n_tok, TPB))),
+                       dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int64_t n4 = n_tok * DIM / 4;
+    hipLaunchKernelGGL(gradq_reduce_kernel, dim3((unsigned)cdiv(n4, 256)), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(a.gq_part), a.gq_slices, n4,
+                       reinterpret_cast<float4*>(a.gQ));
+    return hipGetLastError();
   }
-  if (want_d) {
-    hipError_t e;
-    if (a.Ld <= kSortWavesMaxLd) {
-      const size_t lds = (size_t)(4 * a.Ld + 4) * sizeof(int);
-      hipLaunchKernelGGL(gradd_sort_waves_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
-    } else {
-      const size_t lds = (size_t)(a.Ld + 4) * sizeof(int);
-      hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gradq_kernel<E, DIM>), dim3((unsigned)a.Nq, (unsigned)cdiv(a.Lq, TPB)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <Elem E, int DIM>
+static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t fz_lds, hipStream_t s) {
+  using G = Geo<E, DIM>;
+  constexpr int CPR = G::kCPR;
+  hipError_t e;
+  if (mode == kGdFused) {
+    if (fz_lds > 65536) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gradd_fused_kernel<E, DIM>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)fz_lds);
+      if (e != hipSuccess) return e;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // rows per group: one while groups are scarce; up to 16 (one offsets
-    // load) when the output is large and mostly empty rows
-    const int64_t n_rows = a.n_docs * a.Ld;
-    int rpg = (int)cdiv(n_rows, 256 * 256);
-    const int max_rpg = CPR < 16 ? CPR : 16;   // one offsets load per group
-    rpg = rpg < 1 ? 1 : (rpg > max_rpg ? max_rpg : rpg);
-    const int64_t gpb = 256 / CPR;
-    hipLaunchKernelGGL((gradd_rows_group_kernel<E, DIM>),
-                       dim3((unsigned)cdiv(cdiv(n_rows, rpg), gpb)), dim3(256), 0, s, a, rpg);
-    e = hipGetLastError();
+    hipLaunchKernelGGL((gradd_fused_kernel<E, DIM>), dim3((unsigned)(a.n_docs * a.fz_split)),
+                       dim3(kFzThreads), fz_lds, s, a);
+    return hipGetLastError();
+  }
+  if (mode == kGdPairs) {
+    hipLaunchKernelGGL((gradd_pairs_kernel<E, DIM>), dim3((unsigned)cdiv(a.n_docs, 4)), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+  }
+  if (a.Ld <= kSortWavesMaxLd) {
+    const size_t lds = (size_t)(4 * a.Ld + 4) * sizeof(int);
+    hipLaunchKernelGGL(gradd_sort_waves_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
+  } else {
+    const size_t lds = (size_t)(a.Ld + 4) * sizeof(int);
+    hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // rows per group: one while groups are scarce; up to 16 (one offsets
+  // load) when the output is large and mostly empty rows
+  const int64_t n_rows = a.n_docs * a.Ld;
+  int rpg = (int)cdiv(n_rows, 256 * 256);
+  const int max_rpg = CPR < 16 ? CPR : 16;
+  rpg = rpg < 1 ? 1 : (rpg > max_rpg ? max_rpg : rpg);
+  const int64_t gpb = 256 / CPR;
+  hipLaunchKernelGGL((gradd_rows_group_kernel<E, DIM>),
+                     dim3((unsigned)cdiv(cdiv(n_rows, rpg), gpb)), dim3(256), 0, s, a, rpg);
+  return hipGetLastError();
+}
+
+template <Elem E, int DIM>
+static hipError_t launch_grads(const BwdPlan& p, const BwdArgs& a, bool want_q, bool want_d,
+                               hipStream_t s) {
+  if (want_q) {
+    hipError_t e = launch_gradq<E, DIM>(a, s);
     if (e != hipSuccess) return e;
   }
+  if (want_d) return launch_gradd<E, DIM>(a, p.gd_mode, p.fz_lds, s);
   return hipSuccess;
 }
 
 template <Elem E>
-static hipError_t grads_dim(int dim, const BwdArgs& a, bool wq, bool wd, hipStream_t s) {
-  switch (dim) {
-    case 64: return launch_grads<E, 64>(a, wq, wd, s);
-    case 128: return launch_grads<E, 128>(a, wq, wd, s);
-    case 256: return launch_grads<E, 256>(a, wq, wd, s);
+static hipError_t grads_dim(const BwdPlan& p, const BwdArgs& a, bool wq, bool wd, hipStream_t s) {
+  switch (p.fwd.dim) {
+    case 64: return launch_grads<E, 64>(p, a, wq, wd, s);
+    case 128: return launch_grads<E, 128>(p, a, wq, wd, s);
+    case 256: return launch_grads<E, 256>(p, a, wq, wd, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -696,18 +1025,30 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
   a.sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
   a.sorted_g = reinterpret_cast<float*>(ws + p.off_sorted_g);
   a.roff = reinterpret_cast<int32_t*>(ws + p.off_roff);
+  a.gq_part = reinterpret_cast<float*>(ws + p.off_gq_part);
   a.layout = f.layout;
   a.key_bits = p.key_bits;
+  a.gq_slices = p.gq_slices;
+  a.fz_sw = p.fz_sw;
+  a.fz_split = p.fz_split;
+  a.fz_off_start = p.fz_off_start;
+  a.fz_off_cnt = p.fz_off_cnt;
+  a.fz_off_sorted = p.fz_off_sorted;
+  a.fz_off_gl = p.fz_off_gl;
+  a.fz_off_union = p.fz_off_union;
+  a.fz_off_masks = p.fz_off_masks;
+  a.lq_magic = ((uint64_t(1) << 32) + (uint64_t)f.Lq - 1) / (uint64_t)f.Lq;
   a.Nq = f.Nq;
   a.Lq = f.Lq;
   a.n_docs = f.n_docs;
   a.Ld = f.Ld;
   a.K = f.K;
   a.H = p.H;
+  const bool wq = grad_Q != nullptr, wd = grad_D != nullptr;
   switch (f.elem) {
-    case 0: return grads_dim<Elem::F16>(f.dim, a, grad_Q != nullptr, grad_D != nullptr, s);
-    case 1: return grads_dim<Elem::BF16>(f.dim, a, grad_Q != nullptr, grad_D != nullptr, s);
-    default: return grads_dim<Elem::F32>(f.dim, a, grad_Q != nullptr, grad_D != nullptr, s);
+    case 0: return grads_dim<Elem::F16>(p, a, wq, wd, s);
+    case 1: return grads_dim<Elem::BF16>(p, a, wq, wd, s);
+    default: return grads_dim<Elem::F32>(p, a, wq, wd, s);
   }
 }
 

@@ -39,17 +39,36 @@ struct FwdPlan {
   size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, fwd_bytes = 0;
 };
 
+// grad_D strategies
+enum GdMode : int {
+  kGdSort = 0,    // sort kernel + row kernel through the workspace (any shape)
+  kGdFused = 1,   // all-pairs: one fused kernel per document, sort in LDS
+  kGdPairs = 2    // pairwise / kd: one wave per document streams its rows
+};
+constexpr int kFzThreads = 512;        // threads of the fused grad_D workgroup
+constexpr int kFzMaxHitsPerWave = 2048; // hits one sorting wave of it ranks
+constexpr int kPairsMaxLq = 256;   // longest query of the pairs grad_D kernel
+constexpr int64_t kGqSliceMinDocs = 64;
+
 struct BwdPlan {
   FwdPlan fwd;              // used when the argmax must be recomputed
   bool recompute = false;
   int64_t H = 0;            // hits per document (all-pairs Nq*Lq; pairs Lq)
   int key_bits = 1;
+  int gd_mode = kGdSort;
+  // fused grad_D: sorting waves, workgroups per document, dynamic LDS layout
+  int fz_sw = 0, fz_split = 1;
+  int fz_off_start = 0, fz_off_cnt = 0, fz_off_sorted = 0, fz_off_gl = 0, fz_off_union = 0,
+      fz_off_masks = 0;
+  size_t fz_lds = 0;
+  int gq_slices = 1;        // >1: grad_Q gathered per document slice, then reduced
   size_t off_argmax = 0, off_scores = 0, off_sorted = 0, off_sorted_g = 0, off_roff = 0, off_fwd = 0,
-         total = 0;
+         off_gq_part = 0, total = 0;
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
 // Number of 32-column blocks per wave for an element type and dim.
 inline int blocks_per_wave(int elem, int64_t dim) {
@@ -162,6 +181,50 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
   int bits = 1;
   while (bits < 31 && (int64_t(1) << bits) < Ld) ++bits;
   b.key_bits = bits;
+  // grad_D strategy
+  const int esize = elem == 2 ? 4 : 2;
+  if (layout == kAllPairs && b.H <= 65536 && Ld <= 65535 && Lq > 0 && Ld > 0) {
+    const size_t cpr = (size_t)dim * esize / 16;
+    const size_t ng = kFzThreads / cpr;
+    const size_t part = ng * 2 * (size_t)dim * 4;
+    const size_t keys = align16((size_t)b.H * 2);
+    const size_t start = align16((size_t)(Ld + 1) * 4);
+    const size_t sorted = align16((size_t)b.H * 4);
+    const size_t gl = align16((size_t)f.Nq * 4);
+    // prefer two workgroups per CU (<= 80 KiB), else one (<= 150 KiB)
+    const size_t limits[2] = {80 * 1024, 150 * 1024};
+    for (int li = 0; li < 2 && b.gd_mode == kGdSort; ++li) {
+      for (int sw = kFzThreads / 64; sw >= 1; sw /= 2) {
+        if (cdiv(b.H, sw) > kFzMaxHitsPerWave) break;
+        const size_t cnt = align16((size_t)sw * Ld * 4);
+        const size_t masks = (size_t)sw * Ld * 8;
+        const size_t ph3 = keys + masks;              // keys and masks, then the partials
+        const size_t uni = part > ph3 ? part : ph3;
+        const size_t tot = start + cnt + sorted + gl + uni;
+        if (tot <= limits[li]) {
+          b.gd_mode = kGdFused;
+          b.fz_sw = sw;
+          b.fz_off_start = 0;
+          b.fz_off_cnt = (int)start;
+          b.fz_off_sorted = (int)(start + cnt);
+          b.fz_off_gl = (int)(start + cnt + sorted);
+          b.fz_off_union = (int)(start + cnt + sorted + gl);
+          b.fz_off_masks = (int)(start + cnt + sorted + gl + keys);
+          b.fz_lds = tot;
+          break;
+        }
+      }
+    }
+    if (b.gd_mode == kGdFused) {
+      // enough workgroups to give every CU two
+      int64_t sp = cdiv(512, f.n_docs);
+      b.fz_split = (int)(sp < 1 ? 1 : (sp > 8 ? 8 : sp));
+    }
+  } else if (layout != kAllPairs && Lq > 0 && Lq <= kPairsMaxLq && Ld > 0) {
+    b.gd_mode = kGdPairs;
+  }
+  if (layout == kAllPairs && f.n_docs >= kGqSliceMinDocs && Lq > 0 && Ld > 0) b.gq_slices = 8;
+
   size_t off = 0;
   if (b.recompute && Lq > 0) {
     int64_t pairs = (layout == kAllPairs) ? f.Nq * f.n_docs : f.n_docs;
@@ -172,13 +235,17 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
     b.off_fwd = off;
     off = align256(off + f.fwd_bytes);
   }
-  if (Lq > 0 && Ld > 0) {
+  if (Lq > 0 && Ld > 0 && b.gd_mode == kGdSort) {
     b.off_sorted = off;
     off = align256(off + (size_t)f.n_docs * b.H * 4);
     b.off_sorted_g = off;
     off = align256(off + (size_t)f.n_docs * b.H * 4);
     b.off_roff = off;
     off = align256(off + (size_t)f.n_docs * (Ld + 1) * 4);
+  }
+  if (b.gq_slices > 1) {
+    b.off_gq_part = off;
+    off = align256(off + (size_t)b.gq_slices * f.Nq * Lq * dim * 4);
   }
   b.total = off;
   return b;

@@ -92,7 +92,11 @@ def test_unsupported_dim_is_reported_before_device_work(L):
 def test_backward_rejects_invalid_arguments(L):
     assert bwd(L, g=None) == LIK_ERR_INVALID_ARG
     assert bwd(L, gD=MIS) == LIK_ERR_INVALID_ARG
-    assert bwd(L, wsb=0) == LIK_ERR_INVALID_ARG
+    # without the forward's argmax the backward recomputes it in the workspace
+    need = L.lik_workspace_bytes(LIK_OP_BWD, 2, 32, 3, 40, 128, LIK_BF16, 0)
+    assert need > 0
+    assert bwd(L, argmax=None, wsb=need - 1) == LIK_ERR_INVALID_ARG
+    assert "workspace too small" in L.lik_last_error().decode()
     assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
 
 

@@ -134,6 +134,45 @@ def test_doc_lengths_and_tails(Ld):
     full_check(_custom(f"ld{Ld}-pair", "pairwise", "f16", Q, D[:3], None, None, g[:, 0]))
 
 
+def test_many_documents_grad_q_per_xcd_slice():
+    """Nd >= 64: grad_Q is gathered per document slice (one slice per XCD)
+    and the slice partials are added in order."""
+    rng = np.random.default_rng(1300)
+    Nq, Nd, Lq, Ld, dim = 10, 75, 32, 60, 128
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    D = _rand_tokens(rng, (Nd, Ld, dim))
+    qm = rng.random((Nq, Lq)) < 0.9
+    dm = np.arange(Ld)[None] < rng.integers(1, Ld + 1, Nd)[:, None]
+    dm[17] = False                                   # an empty document
+    g = rng.standard_normal((Nq, Nd))
+    full_check(_custom("many-docs", "allpairs", "bf16", Q, D, qm, dm, g))
+
+
+def test_hub_rows_collect_most_hits():
+    """A few document rows are the argmax of almost every query token, so a
+    row's sorted hits span many lane groups and its gradient row is put
+    together from their partials; duplicated hub tokens tie exactly and the
+    lower index takes the hits.  Rows with no hit stay exactly zero."""
+    rng = np.random.default_rng(1400)
+    Nq, Nd, Lq, Ld, dim = 48, 3, 32, 90, 128
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    Q[..., 0] = np.abs(Q[..., 0]) + 1.0
+    Q /= np.linalg.norm(Q, axis=-1, keepdims=True)
+    D = 0.3 * _rand_tokens(rng, (Nd, Ld, dim))
+    hub = np.zeros(dim, np.float32)
+    hub[0] = 1.0
+    D[0, 7] = hub
+    D[1, 3] = hub
+    D[1, 50] = hub                                   # exact duplicate: ties go to row 3
+    D[2, 80] = hub
+    D[2, 81] = 0.5 * hub
+    g = rng.standard_normal((Nq, Nd))
+    w = _custom("hubs", "allpairs", "bf16", Q, D, None, None, g)
+    full_check(w)
+    s, a = gpu_forward(w)
+    assert np.mean(a[:, 0] == 7) > 0.9 and np.all(a[:, 1] != 50)
+
+
 def test_arbitrary_masks_and_degenerate_rows():
     """Scattered (not suffix) masks, fully masked tiles inside a document, an
     empty document, an empty query, and a document whose valid similarities
