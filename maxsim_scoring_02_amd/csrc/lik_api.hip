@@ -109,6 +109,10 @@ lik_status check_supported(lik_dtype dtype, const Shapes& s) {
   if (s.dim == 0 || !lik::fwd_dim_supported(s.dim))
     return fail(LIK_ERR_UNSUPPORTED, "embedding dim %lld has no kernel in this build (64, 128, 256)",
                 (long long)s.dim);
+  if (s.layout == lik::kAllPairs && (s.nd_or_n > lik::kApMaxDocIndex || s.Ld > lik::kApMaxLd))
+    return fail(LIK_ERR_UNSUPPORTED, "all-pairs supports Nd <= %lld and Ld <= %lld (got %lld, %lld)",
+                (long long)lik::kApMaxDocIndex, (long long)lik::kApMaxLd, (long long)s.nd_or_n,
+                (long long)s.Ld);
   return LIK_OK;
 }
 

@@ -125,6 +125,19 @@ __device__ __forceinline__ void tile_mask(f32x16& acc, uint32_t word, int h) {
   }
 }
 
+// Initial accumulator of a tile that is not fully valid: 0 in the rows the
+// validity word keeps, -inf in the others (-inf + finite products stays
+// -inf, so a masked row never wins a max).  `word` bit r = row r valid.
+__device__ __forceinline__ void tile_init(f32x16& c, uint32_t word, int h) {
+  const uint32_t w = word >> (4 * h);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int bit = 8 * (v >> 2) + (v & 3);
+    const int keep = (int)(w << (31 - bit)) >> 31;     // -1 valid, 0 masked
+    c[v] = __int_as_float(~keep & (int)0xff800000u);
+  }
+}
+
 // Fold one (masked) tile's accumulator into the running state, branch-free.
 // Strict '>' keeps the earlier tile on ties, so tiles must come in order.
 __device__ __forceinline__ void state_fold(BlockState& s, const f32x16& acc, int t) {
@@ -271,6 +284,21 @@ __device__ __forceinline__ float segmented_scan(float v, int lane_in, int seg_st
     float t = __shfl_up(v, k, WIDTH);
     if (lane_in - k >= seg_start) v += t;
   }
+  return v;
+}
+
+// Sum of v over lanes 0..31 (returned in lane 31) and over lanes 32..63
+// (returned in lane 63), by DPP row shifts and a row broadcast: no LDS.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float half_sum32(float v) {
+  v += dpp_f32<0x111, 0xf>(v);   // row_shr:1
+  v += dpp_f32<0x112, 0xf>(v);   // row_shr:2
+  v += dpp_f32<0x114, 0xf>(v);   // row_shr:4
+  v += dpp_f32<0x118, 0xf>(v);   // row_shr:8  -> lane 15 of each row holds its row sum
+  v += dpp_f32<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
   return v;
 }
 

@@ -129,6 +129,26 @@ __device__ __forceinline__ void mfma_tile_pad(f32x16 (&acc)[NB], const char* buf
   }
 }
 
+// acc = C + A * B over one tile, with C the tile's initial value (zero, or
+// -inf in the rows a mask removes).
+template <Elem E, int DIM, int NB>
+__device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
+                                            const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
+                                            int a_off, const f32x16& c0) {
+  using G = Geo<E, DIM>;
+#pragma unroll
+  for (int m = 0; m < G::kKSteps; ++m) {
+    const u32x4 av = ld_lds_16(buf, a_off + m * 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (m == 0) {
+        acc[b] = c0;
+      }
+      mfma_chunk<E>(acc[b], av, bf[b][m]);
+    }
+  }
+}
+
 template <Elem E, int DIM, int NB, bool MASK>
 __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   using G = Geo<E, DIM>;
@@ -160,6 +180,64 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   const int gw = sb * kApNW + wave;
   const bool active = gw < a.n_cg;
 
+  // ---- the workgroup's units (document, chunk) and their super-tiles ----
+  // A flat schedule in LDS: entry e = one super-tile (or one empty unit),
+  // with its tile index, validity words and start/end-of-unit flags, so the
+  // hot loop below holds no cursor arithmetic and no global index loads.
+  const int nchunks = (int)a.nchunks, tpc = (int)a.tpc;
+  const int64_t n_units = a.n_docs * a.nchunks;
+  const int64_t u_begin = (int64_t)g * a.upw;
+  const int n_my = (int)(min(u_begin + a.upw, n_units) - u_begin);
+  const int Ld = (int)a.Ld;
+  __shared__ int s_meta[kApMaxST];     // t | two << 24 | start << 25 | end << 26 | has << 27
+  __shared__ int s_unit[kApMaxST];     // d << 8 | chunk
+  __shared__ uint32_t s_w0[kApMaxST], s_w1[kApMaxST];
+  __shared__ int s_uoff[kApMaxDocs + 1], s_ut0[kApMaxDocs], s_ut1[kApMaxDocs];
+  if (wave == 0) {
+    int nst = 0, t0 = 0, t1 = 0;
+    if (lane < n_my) {
+      const int64_t u = u_begin + lane;
+      const int d = (int)(u / nchunks), c = (int)(u - (int64_t)d * nchunks);
+      const int nt = MASK ? a.ntiles[d] : (int)a.ntiles_max;
+      t0 = c * tpc;
+      t1 = min(t0 + tpc, nt);
+      if (t1 < t0) t1 = t0;
+      nst = t1 > t0 ? (t1 - t0 + 1) / 2 : 1;    // an empty unit still flushes
+    }
+    int incl = nst;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane < n_my) {
+      s_uoff[lane] = incl - nst;
+      s_ut0[lane] = t0;
+      s_ut1[lane] = t1;
+    }
+    if (lane == 63) s_uoff[kApMaxDocs] = incl;
+  }
+  __syncthreads();
+  for (int x = tid; x < n_my * 32; x += kApThreads) {
+    const int k = x >> 5, j = x & 31;
+    const int t0 = s_ut0[k], t1 = s_ut1[k], off = s_uoff[k];
+    const int nst = t1 > t0 ? (t1 - t0 + 1) / 2 : 1;
+    if (j < nst) {
+      const int64_t u = u_begin + k;
+      const int d = (int)(u / nchunks), c = (int)(u - (int64_t)d * nchunks);
+      const int t = t0 + 2 * j;
+      const bool has = t < t1, two = t + 1 < t1;
+      uint32_t w0 = 0u, w1 = 0u;
+      if (has) w0 = MASK ? a.bits[(int64_t)d * a.nwords + t] : tile_word(nullptr, t, Ld);
+      if (two) w1 = MASK ? a.bits[(int64_t)d * a.nwords + t + 1] : tile_word(nullptr, t + 1, Ld);
+      s_w0[off + j] = w0;
+      s_w1[off + j] = w1;
+      s_meta[off + j] = t | ((int)two << 24) | ((int)(j == 0) << 25) | ((int)(j == nst - 1) << 26) |
+                        ((int)has << 27);
+      s_unit[off + j] = (d << 8) | c;
+    }
+  }
+
   // query fragments of this wave's slots (B operand), kept for all units
   u32x4 bf[NB][G::kKSteps];
   {
@@ -181,66 +259,31 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   const bool slot_tok = slot_ok && (!a.q_mask || a.q_mask[slot_q * a.Lq + slot_i]);
   const int seg_start = a.qpw > 0 ? (int)((L / a.Lq) * a.Lq) : 0;
   const bool seg_last = slot_ok && slot_i == a.Lq - 1;
-
-  // Units u = d * nchunks + c of this workgroup: [u_begin, u_end).  (d, c)
-  // are stepped incrementally; tile counts are uniform (readfirstlane).
-  const int nchunks = (int)a.nchunks, tpc = (int)a.tpc;
-  const int64_t n_units = a.n_docs * a.nchunks;
-  const int64_t u_begin = (int64_t)g * a.upw;
-  const int n_my = (int)(min(u_begin + a.upw, n_units) - u_begin);
-  const int d_begin = (int)(u_begin / nchunks), c_begin = (int)(u_begin % nchunks);
-  const int ntiles_full = (int)a.ntiles_max;
-  auto doc_tiles = [&](int d) -> int {
-    return MASK ? __builtin_amdgcn_readfirstlane(a.ntiles[d]) : ntiles_full;
-  };
-  auto chunk_range = [&](int nt, int c, int& t0, int& t1) {
-    t0 = c * tpc;
-    t1 = min(t0 + tpc, nt);
-    if (t1 < t0) t1 = t0;
-  };
-
-  // load cursor: the next super-tile to bring into LDS, in consumption order
-  int pk = 0, pd = d_begin, pc = c_begin, pnt = doc_tiles(d_begin), pt = 0, pt1 = 0;
-  bool have = false;
-  for (; pk < n_my;) {
-    chunk_range(pnt, pc, pt, pt1);
-    if (pt < pt1) { have = true; break; }
-    ++pk;
-    if (++pc == nchunks) { pc = 0; ++pd; if (pk < n_my) pnt = doc_tiles(pd); }
-  }
-  // When nothing follows, the cursor stays on the last super-tile (the
-  // prefetch then re-reads it from L2 and the copy is not stored).
-  auto advance = [&]() {
-    if (pt + kSub < pt1) {
-      pt += kSub;
-      return true;
-    }
-    int k = pk, d = pd, c = pc, nt = pnt;
-    while (k + 1 < n_my) {
-      ++k;
-      if (++c == nchunks) { c = 0; ++d; nt = doc_tiles(d); }
-      int t0, t1;
-      chunk_range(nt, c, t0, t1);
-      if (t0 < t1) {
-        pk = k; pd = d; pc = c; pnt = nt; pt = t0; pt1 = t1;
-        return true;
-      }
-    }
-    return false;
-  };
+  // queries of 32 tokens two to a wave: their sums are lane-aligned halves
+  const bool fast_sum = a.qpw > 0 && a.Lq == 32;
+  const int64_t score_base = slot_q * a.n_docs;
+  const int64_t part_lane = (int64_t)gw * SPW + L;
+  __syncthreads();
+  const int S = s_uoff[kApMaxDocs];
 
   // per-thread load/store geometry: chunk tid + k*256 of the super-tile
   const int lrow = tid / G::kCPR, lcol = tid - lrow * G::kCPR;
   const int st_off = lrow * PD::kStride + lcol * 16;
   u32x4 pre[kLoads];
-  auto gload = [&]() {
-    const char* base = (const char*)a.D + ((int64_t)pd * a.Ld + (int64_t)pt * kTile) * G::kRowBytes;
-    const int rows = min(pt1 * kTile, (int)a.Ld) - pt * kTile;
-    const int nbytes = min(rows, kSTRows) * G::kRowBytes;
+  // Super-tile loads: one buffer descriptor per step keeps the per-lane
+  // offset constant and makes the range check (which covers the per-lane
+  // offset only) exact; rows past the unit read as zeros.
+  auto gload = [&](int e) {
+    const int meta = __builtin_amdgcn_readfirstlane(s_meta[e]);
+    const int unit = __builtin_amdgcn_readfirstlane(s_unit[e]);
+    const int d = unit >> 8, c = unit & 0xff;
+    const int t = meta & 0xffffff;
+    const int t1 = min(c * tpc + tpc, (int)a.ntiles_max);
+    const char* base = (const char*)a.D + ((int64_t)d * Ld + (int64_t)t * kTile) * G::kRowBytes;
+    const int rows = min(t1 * kTile, Ld) - t * kTile;
+    const int nbytes = ((meta >> 27) & 1) ? min(rows, kSTRows) * G::kRowBytes : 0;
 #pragma unroll
     for (int k = 0; k < kLoads; ++k) {
-      // one descriptor per step keeps the per-lane offset constant and the
-      // range check (which covers the per-lane offset only) exact
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(base + k * kBytesPerLoad), 0, max(nbytes - k * kBytesPerLoad, 0), 0x00020000);
       pre[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, 0, 0);
@@ -252,86 +295,75 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   };
 
   int cur = 0;
-  if (have) {
-    gload();
+  if (S > 0) {
+    gload(0);
     lstore(lds);
   }
   __syncthreads();
 
   const int a_off = r * PD::kStride + h * 16;
   f32x16 X[NB];
-  int cd = d_begin, cc = c_begin, cnt = doc_tiles(d_begin);
-  for (int k = 0; k < n_my; ++k) {
-    if (k > 0 && ++cc == nchunks) {
-      cc = 0;
-      ++cd;
-      cnt = doc_tiles(cd);
+  BlockState st[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) state_init(st[b], 0);
+  for (int e = 0; e < S; ++e) {
+    const int meta = __builtin_amdgcn_readfirstlane(s_meta[e]);
+    const uint32_t word0 = __builtin_amdgcn_readfirstlane(s_w0[e]);
+    const uint32_t word1 = __builtin_amdgcn_readfirstlane(s_w1[e]);
+    const int t = meta & 0xffffff;
+    const bool two = (meta >> 24) & 1, ustart = (meta >> 25) & 1, uend = (meta >> 26) & 1;
+    const bool has = (meta >> 27) & 1;
+    // the next entry's tiles are loaded now (the last entry reloads its own)
+    const bool nxt = e + 1 < S;
+    gload(nxt ? e + 1 : e);
+    if (ustart) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) state_init(st[b], t);
     }
-    int t0, t1;
-    chunk_range(cnt, cc, t0, t1);
-    const uint32_t* bits_d = MASK ? a.bits + (int64_t)cd * a.nwords : nullptr;
-    BlockState st[NB];
+    if (active && has) {
+      const char* buf = lds + cur * kSTBytes;
+      mfma_tile_pad<E, DIM, NB>(X, buf, bf, a_off);
+      if (word0 != kFull) tiles_mask<NB>(X, word0, h);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) state_init(st[b], t0);
-
-    for (int t = t0; t < t1; t += kSub) {
-      // tile words are read before the prefetch is issued: loads retire in
-      // order, so a word read after it would also wait for the prefetch
-      uint32_t word0, word1;
-      if constexpr (MASK) {
-        word0 = __builtin_amdgcn_readfirstlane(bits_d[t]);
-        word1 = __builtin_amdgcn_readfirstlane(bits_d[min(t + 1, t1 - 1)]);
-      } else {
-        word0 = tile_word(nullptr, t, a.Ld);
-        word1 = tile_word(nullptr, t + 1, a.Ld);
+      for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t);
+      if (two) {
+        mfma_tile_pad<E, DIM, NB>(X, buf + PD::kTileBytes, bf, a_off);
+        if (word1 != kFull) tiles_mask<NB>(X, word1, h);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t + 1);
       }
-      const bool two = t + 1 < t1;
-      // inside the loop a tile exists, so the cursor is valid
-      const bool nxt = advance();
-      gload();
-      if (active) {
-        const char* buf = lds + cur * kSTBytes;
-        mfma_tile_pad<E, DIM, NB>(X, buf, bf, a_off);
-        if (word0 != kFull) tiles_mask<NB>(X, word0, h);
+    }
+    if (nxt) lstore(lds + (cur ^ 1) * kSTBytes);
+    if (uend && active) {
+      // flush this unit
+      const int unit = __builtin_amdgcn_readfirstlane(s_unit[e]);
+      const int cd = unit >> 8, cc = unit & 0xff;
+      float M[NB];
+      int J[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t);
-        if (two) {
-          mfma_tile_pad<E, DIM, NB>(X, buf + PD::kTileBytes, bf, a_off);
-          if (word1 != kFull) tiles_mask<NB>(X, word1, h);
-#pragma unroll
-          for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t + 1);
+      for (int b = 0; b < NB; ++b) state_resolve(st[b], h, M[b], J[b]);
+      float Mv;
+      int Jv;
+      combine_halves<NB>(M, J, lane, Mv, Jv);
+      if (a.partial) {
+        if (writer) {
+          const int64_t idx = ((int64_t)cc * a.n_docs + cd) * a.n_cg * SPW + part_lane;
+          a.part_M[idx] = has ? Mv : -__builtin_inff();
+          a.part_J[idx] = has ? Jv : -1;
+        }
+      } else {
+        const bool empty = !has;          // single chunk: no tile means no valid token
+        const float v = slot_tok ? Mv : 0.0f;
+        const float sc = fast_sum ? half_sum32(v) : segmented_scan<SPW>(v, L, seg_start);
+        if (slot_ok && writer) {
+          const int64_t pair = score_base + cd;
+          if (seg_last) a.scores[pair] = empty ? kEmptyDocScore : sc;
+          if (a.argmax) a.argmax[pair * a.Lq + slot_i] = (slot_tok && !empty) ? Jv : -1;
         }
       }
-      if (nxt) lstore(lds + (cur ^ 1) * kSTBytes);
-      __syncthreads();
-      cur ^= 1;
     }
-
-    if (!active) continue;
-    // flush this unit
-    float M[NB];
-    int J[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) state_resolve(st[b], h, M[b], J[b]);
-    float Mv;
-    int Jv;
-    combine_halves<NB>(M, J, lane, Mv, Jv);
-    if (a.partial) {
-      const bool any = t1 > t0;
-      if (writer) {
-        const int64_t idx = (((int64_t)cc * a.n_docs + cd) * a.n_cg + gw) * SPW + L;
-        a.part_M[idx] = any ? Mv : -__builtin_inff();
-        a.part_J[idx] = any ? Jv : -1;
-      }
-    } else {
-      const bool empty = t1 == 0;   // single chunk: t1 is the doc's tile count
-      const float s = segmented_scan<SPW>(slot_tok ? Mv : 0.0f, L, seg_start);
-      if (slot_ok && writer) {
-        const int64_t pair = slot_q * a.n_docs + cd;
-        if (seg_last) a.scores[pair] = empty ? kEmptyDocScore : s;
-        if (a.argmax) a.argmax[pair * a.Lq + slot_i] = (slot_tok && !empty) ? Jv : -1;
-      }
-    }
+    __syncthreads();
+    cur ^= 1;
   }
 }
 

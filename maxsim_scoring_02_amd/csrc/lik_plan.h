@@ -67,6 +67,17 @@ struct BwdPlan {
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// all-pairs forward: a workgroup's units span at most kApMaxDocs documents
+// and kApMaxWords tile words (their counts and words are kept in LDS)
+constexpr int kApMaxDocs = 64;
+constexpr int kApMaxWords = 1024;
+// all-pairs schedule entries pack (document << 8 | chunk): documents below
+// 2^23, chunks of 1024 rows below 256
+constexpr int64_t kApMaxDocIndex = (int64_t(1) << 23) - 1;
+constexpr int64_t kApMaxLd = 255 * 1024;
+// schedule entries: a super-tile (2 tiles) each, or one per empty unit
+constexpr int kApMaxST = kApMaxWords / 2 + 2 * kApMaxDocs;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
@@ -144,6 +155,10 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
     int64_t per_sb = cdiv(target, p.n_sb);
     p.upw = per_sb >= units ? 1 : cdiv(units, per_sb);
     if (p.upw < 1) p.upw = 1;
+    const int64_t cap_docs = (kApMaxDocs - 1) * p.nchunks;
+    const int64_t cap_words = kApMaxWords / p.tpc;
+    if (p.upw > cap_docs) p.upw = cap_docs;
+    if (p.upw > cap_words) p.upw = cap_words;
     p.n_groups = cdiv(units, p.upw);
     p.gpx = cdiv(p.n_groups, 8);
   } else {
