@@ -100,6 +100,18 @@ const char* lik_last_error(void);
 int lik_supported_dim(int64_t dim);
 
 /*
+ * Profiling hook (not needed for scoring).  After this call, every forward
+ * entry point called from the same host thread records `start_event` on its
+ * stream just before it launches its main scoring kernel and `stop_event`
+ * just after it (the mask preparation and split-merge kernels fall outside),
+ * so that the main kernel's duration can be read with hipEventElapsedTime.
+ * Both are hipEvent_t handles owned by the caller, created on the current
+ * device; pass NULL, NULL to stop.  Returns LIK_ERR_INVALID_ARG when exactly
+ * one of them is NULL.
+ */
+lik_status lik_set_profile_events(void* start_event, void* stop_event);
+
+/*
  * Workspace bytes needed by one call.  Arguments mirror the entry point:
  *   all-pairs : nq_or_b = Nq, nd_or_n = Nd;
  *   pairwise  : nq_or_b = B,  nd_or_n = 1 (ignored);

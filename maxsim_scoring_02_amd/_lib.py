@@ -45,6 +45,7 @@ SIGNATURES = {
     "lik_status_string": ([_I], ctypes.c_char_p),
     "lik_last_error": ([], ctypes.c_char_p),
     "lik_supported_dim": ([_I64], _I),
+    "lik_set_profile_events": ([_P, _P], _I),
     "lik_workspace_bytes": ([_I, _I64, _I64, _I64, _I64, _I64, _I, _I], _SZ),
     "lik_maxsim_fwd": (_FWD_ALLPAIRS, _I),
     "lik_maxsim_bwd": (_BWD_ALLPAIRS, _I),

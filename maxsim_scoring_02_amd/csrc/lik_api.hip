@@ -19,6 +19,7 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 lik_status fail(lik_status s, const char* fmt, ...) {
   va_list ap;
@@ -188,6 +189,13 @@ lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dt
 
 }  // namespace
 
+namespace lik {
+void profile_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_prof_start;
+  *stop = g_prof_stop;
+}
+}  // namespace lik
+
 extern "C" {
 
 int lik_abi_version(void) { return LIK_ABI_VERSION; }
@@ -205,6 +213,14 @@ const char* lik_status_string(lik_status s) {
 const char* lik_last_error(void) { return g_last_error; }
 
 int lik_supported_dim(int64_t dim) { return lik::fwd_dim_supported(dim) ? 1 : 0; }
+
+lik_status lik_set_profile_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(LIK_ERR_INVALID_ARG, "profile events: pass both or neither");
+  g_prof_start = static_cast<hipEvent_t>(start_event);
+  g_prof_stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
 
 size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or_n, int64_t ld,
                            int64_t dim, lik_dtype dtype, int flags) {

@@ -543,6 +543,12 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
 template <Elem E, int DIM, int NB, bool MASK>
 static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
+  hipEvent_t ev0, ev1;
+  profile_events(&ev0, &ev1);
+  if (ev0) {
+    hipError_t e = hipEventRecord(ev0, s);
+    if (e != hipSuccess) return e;
+  }
   if (p.layout == kAllPairs) {
     const int64_t grid = 8 * p.gpx * p.n_sb;
     constexpr int lds = ap_lds_bytes<E, DIM>();
@@ -560,7 +566,9 @@ static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t 
     hipLaunchKernelGGL((pairs_fwd_kernel<E, DIM, NB, MASK>), dim3((unsigned)grid),
                        dim3(W * kWave), W * G::kTileBytes, s, a);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
+  return e;
 }
 
 template <Elem E, int DIM, int NB>

@@ -29,6 +29,10 @@ struct FwdArgs {
 
 bool fwd_dim_supported(int64_t dim);
 
+// Events the caller asked to have recorded around the main forward kernel
+// (null when not profiling); see lik_set_profile_events.
+void profile_events(hipEvent_t* start, hipEvent_t* stop);
+
 hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uint8_t* q_mask,
                        const uint8_t* d_mask, float* scores, int32_t* argmax, char* ws,
                        hipStream_t s);

@@ -26,10 +26,16 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = _lib.header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), f"liblik.so does not export {n}"
     assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_profile_events_need_both_or_neither(L):
+    assert L.lik_set_profile_events(None, FAKE) == LIK_ERR_INVALID_ARG
+    assert L.lik_set_profile_events(FAKE, None) == LIK_ERR_INVALID_ARG
+    assert L.lik_set_profile_events(None, None) == LIK_OK
 
 
 def test_version_and_status_strings(L):
