@@ -68,8 +68,9 @@ def _valid_lengths(w):
     return qv.astype(np.int64), dv.astype(np.int64)
 
 
-def work(w):
-    """(forward flops, backward flops, forward bytes, backward bytes)."""
+def work(w, keep_argmax=True):
+    """(forward flops, backward flops, forward bytes, backward bytes).  The
+    forward writes the int32 argmax only when it is kept (training)."""
     dim = w.dim
     eb = w.Q.element_size()
     qv, dv = _valid_lengths(w)
@@ -90,7 +91,7 @@ def work(w):
     d_bytes = float(dv.sum() * dim * eb)
     mask_bytes = (0 if w.q_mask is None else w.q_mask.numel()) + \
                  (0 if w.d_mask is None else w.d_mask.numel())
-    b_fwd = q_bytes + d_bytes + mask_bytes + n_scores * 4 + n_scores * Lq * 4
+    b_fwd = q_bytes + d_bytes + mask_bytes + n_scores * 4 + (n_scores * Lq * 4 if keep_argmax else 0)
     d_rows = float(np.prod(w.D.shape[:-1]))
     b_bwd = (q_bytes + d_bytes + n_scores * 4 + n_scores * Lq * 4
              + w.Q.shape[0] * Lq * dim * 4 + d_rows * dim * 4)
@@ -120,7 +121,9 @@ class Op:
         Lq, dim = w.Q.shape[1], w.dim
         shape = w.scores_shape
         self.scores = torch.empty(shape, dtype=torch.float32, device=dev)
-        self.argmax = torch.empty(tuple(shape) + (Lq,), dtype=torch.int32, device=dev)
+        # scoring-only workloads (no backward) do not keep the argmax
+        self.argmax = (torch.empty(tuple(shape) + (Lq,), dtype=torch.int32, device=dev)
+                       if backward else None)
         lay = w.layout
         if lay == "allpairs":
             self.dims = (w.Q.shape[0], Lq, w.D.shape[0], w.D.shape[1], dim)
@@ -131,9 +134,10 @@ class Op:
         else:
             self.dims = (w.Q.shape[0], Lq, w.D.shape[1], w.D.shape[2], dim)
             ops = (_lib.LIK_OP_KD_FWD, _lib.LIK_OP_KD_BWD)
-        flags = 1 | (2 if self.dm is not None else 0)
-        self.wsf_n = self.L.lik_workspace_bytes(ops[0], *self.dims, self.dt, flags)
-        self.wsb_n = self.L.lik_workspace_bytes(ops[1], *self.dims, self.dt, flags)
+        flags_f = (1 if self.argmax is not None else 0) | (2 if self.dm is not None else 0)
+        flags_b = 1 | (2 if self.dm is not None else 0)
+        self.wsf_n = self.L.lik_workspace_bytes(ops[0], *self.dims, self.dt, flags_f)
+        self.wsb_n = self.L.lik_workspace_bytes(ops[1], *self.dims, self.dt, flags_b)
         mk = lambda n: torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         self.wsf = mk(self.wsf_n)
         self.wsb = mk(self.wsb_n)
@@ -353,7 +357,7 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
 
     w, backward = make_workload(name)
     op = Op(w, backward)
-    f_fwd, f_bwd, b_fwd, b_bwd = work(w)
+    f_fwd, f_bwd, b_fwd, b_bwd = work(w, keep_argmax=backward)
     for _ in range(warmup):
         op.fwd()
         if backward:

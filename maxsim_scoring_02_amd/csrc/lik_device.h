@@ -179,10 +179,8 @@ __device__ __forceinline__ void tiles_mask(f32x16 (&acc)[NB], uint32_t word, int
     for (int v = 0; v < 16; ++v) acc[b][v] = ok[v] ? acc[b][v] : -__builtin_inff();
 }
 
-// Fold a masked tile into the running state.  The copy of the tile's values
-// runs only in the lanes whose maximum improved (strict '>': the earlier tile
-// keeps ties), and is skipped by the whole wave when no lane improved.
-__device__ __forceinline__ void state_fold_sparse(BlockState& s, const f32x16& acc, int t) {
+// Largest of a lane's 16 accumulator values (a tree of 3-input maxima).
+__device__ __forceinline__ float max16(const f32x16& acc) {
   const float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
   const float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
   const float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
@@ -190,7 +188,30 @@ __device__ __forceinline__ void state_fold_sparse(BlockState& s, const f32x16& a
   const float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
   const float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
   const float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
-  const float tmax = __builtin_fmaxf(m1, m2);
+  return __builtin_fmaxf(m1, m2);
+}
+
+// Fold two consecutive tiles (t, t+1) at once: one comparison with the
+// running max and at most one copy of 16 values, from the tile holding the
+// pair's maximum (the earlier tile on ties).
+__device__ __forceinline__ void state_fold_pair(BlockState& s, const f32x16& xa,
+                                                const f32x16& xb, int t) {
+  const float ta = max16(xa), tb = max16(xb);
+  const float tm = __builtin_fmaxf(ta, tb);
+  if (tm > s.run_max) {
+    s.run_max = tm;
+    const bool useb = tb > ta;
+    s.best_tile = useb ? t + 1 : t;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s.best_val[v] = useb ? xb[v] : xa[v];
+  }
+}
+
+// Fold a masked tile into the running state.  The copy of the tile's values
+// runs only in the lanes whose maximum improved (strict '>': the earlier tile
+// keeps ties), and is skipped by the whole wave when no lane improved.
+__device__ __forceinline__ void state_fold_sparse(BlockState& s, const f32x16& acc, int t) {
+  const float tmax = max16(acc);
   if (tmax > s.run_max) {
     s.run_max = tmax;
     s.best_tile = t;

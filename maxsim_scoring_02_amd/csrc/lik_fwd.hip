@@ -94,6 +94,10 @@ __device__ __forceinline__ void load_bfrags(u32x4 (&bf)[NB][KS], const char* Qb,
   }
 }
 
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
 // ---------------------------------------------------------------------------
 // all-pairs forward
 //
@@ -109,9 +113,16 @@ constexpr int kApNW = 4;                       // waves per workgroup
 constexpr int kApThreads = kApNW * kWave;
 constexpr int kSub = 2;                        // tiles per super-tile
 
+// LDS buffers of super-tiles: three (loads run two super-tiles ahead) when
+// they fit in 64 KB, else two (one ahead)
+template <Elem E, int DIM>
+constexpr int ap_stages() {
+  return 3 * kSub * Pad<E, DIM>::kTileBytes <= 65536 ? 3 : 2;
+}
+
 template <Elem E, int DIM>
 constexpr int ap_lds_bytes() {
-  return 2 * kSub * Pad<E, DIM>::kTileBytes;
+  return ap_stages<E, DIM>() * kSub * Pad<E, DIM>::kTileBytes;
 }
 
 template <Elem E, int DIM, int NB>
@@ -149,7 +160,8 @@ __device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
   }
 }
 
-template <Elem E, int DIM, int NB, bool MASK>
+// KEEP: the caller wants the argmax; without it only running maxima are kept.
+template <Elem E, int DIM, int NB, bool MASK, bool KEEP>
 __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   using G = Geo<E, DIM>;
   using PD = Pad<E, DIM>;
@@ -169,13 +181,14 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; give every doc
-  // group a fixed XCD so its tiles stay in that XCD's L2 across slot blocks.
+  // Workgroups are dispatched round-robin over the 8 XCDs.  Every doc group
+  // has a fixed XCD, and its slot blocks are dispatched back to back there,
+  // so they run together and each tile comes from HBM once, then from L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, kx = bid >> 3;
-  const int gpx = (int)a.gpx;
-  const int g = xcd + 8 * (kx % gpx);
-  const int sb = kx / gpx;
+  const int n_sb = (int)a.n_sb;
+  const int g = xcd + 8 * (kx / n_sb);
+  const int sb = kx - (kx / n_sb) * n_sb;
   if (g >= a.n_groups || sb >= a.n_sb) return;
   const int gw = sb * kApNW + wave;
   const bool active = gw < a.n_cg;
@@ -266,82 +279,160 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   __syncthreads();
   const int S = s_uoff[kApMaxDocs];
 
-  // per-thread load/store geometry: chunk tid + k*256 of the super-tile
-  const int lrow = tid / G::kCPR, lcol = tid - lrow * G::kCPR;
-  const int st_off = lrow * PD::kStride + lcol * 16;
-  u32x4 pre[kLoads];
-  // Super-tile loads: one buffer descriptor per step keeps the per-lane
-  // offset constant and makes the range check (which covers the per-lane
-  // offset only) exact; rows past the unit read as zeros.
-  auto gload = [&](int e) {
-    const int meta = __builtin_amdgcn_readfirstlane(s_meta[e]);
-    const int unit = __builtin_amdgcn_readfirstlane(s_unit[e]);
+  // Super-tiles are copied global -> LDS directly (no registers): the padded
+  // super-tile is kBlocks blocks of 1 KB, block q written by wave q % 4 as its
+  // (q / 4)-th load, lane l landing at byte 16 l of the block.  A lane's
+  // global offset inside the super-tile follows from that LDS position;
+  // lanes that land on row padding re-read offset 0.  One buffer descriptor
+  // per super-tile bounds the reads to the unit's rows (the rest read zero).
+  constexpr int kBlocks = kSTBytes / 1024;
+  static_assert(kSTBytes % 1024 == 0, "padded super-tile must be whole 1 KB blocks");
+  constexpr int kMyLoads = (kBlocks + kApNW - 1) / kApNW;   // per wave, at most
+  const int my_loads = (kBlocks - wave + kApNW - 1) / kApNW;
+  uint32_t voff[kMyLoads];
+#pragma unroll
+  for (int i = 0; i < kMyLoads; ++i) {
+    const int q = i * kApNW + wave;
+    const int bt = q * 1024 + lane * 16;                // byte in the padded super-tile
+    const int tile = bt / PD::kTileBytes, o = bt - tile * PD::kTileBytes;
+    const int row = o / PD::kStride, cb = o - row * PD::kStride;
+    voff[i] = (q < kBlocks && cb < G::kRowBytes)
+                  ? (uint32_t)((tile * kTile + row) * G::kRowBytes + cb)
+                  : 0u;
+  }
+  auto gload = [&](int meta, int unit, int stage) {
     const int d = unit >> 8, c = unit & 0xff;
     const int t = meta & 0xffffff;
     const int t1 = min(c * tpc + tpc, (int)a.ntiles_max);
     const char* base = (const char*)a.D + ((int64_t)d * Ld + (int64_t)t * kTile) * G::kRowBytes;
     const int rows = min(t1 * kTile, Ld) - t * kTile;
     const int nbytes = ((meta >> 27) & 1) ? min(rows, kSTRows) * G::kRowBytes : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+    char* dst = lds + stage * kSTBytes;
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(base + k * kBytesPerLoad), 0, max(nbytes - k * kBytesPerLoad, 0), 0x00020000);
-      pre[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, 0, 0);
+    for (int i = 0; i < kMyLoads; ++i) {
+      if (i < my_loads)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + (i * kApNW + wave) * 1024), 16,
+            (int)voff[i], 0, 0, 0);
     }
   };
-  auto lstore = [&](char* buf) {
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) st_lds_16(buf, st_off + k * kRowsPerLoad * PD::kStride, pre[k]);
+  constexpr int NST = ap_stages<E, DIM>();
+  // wait until this wave's loads for the next entry are in LDS (with three
+  // stages the loads issued this step, for the entry after, stay in flight)
+  auto wait_stage = [&]() {
+    if constexpr (NST == 3) {
+      if (my_loads == kMyLoads) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads - 1));
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
   };
 
-  int cur = 0;
-  if (S > 0) {
-    gload(0);
-    lstore(lds);
+  if (S > 0) gload(__builtin_amdgcn_readfirstlane(s_meta[0]), __builtin_amdgcn_readfirstlane(s_unit[0]), 0);
+  if (NST == 3 && S > 1) {
+    gload(__builtin_amdgcn_readfirstlane(s_meta[1]), __builtin_amdgcn_readfirstlane(s_unit[1]), 1);
+    wait_stage();
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
   __syncthreads();
 
   const int a_off = r * PD::kStride + h * 16;
-  f32x16 X[NB];
+  f32x16 Xa[NB], Xb[NB];
+  // One tile's similarities; a tile that is not fully valid starts its
+  // masked rows at -inf (-inf plus finite products stays -inf, so they
+  // never win a max), a full tile starts from zero.
+  auto tile_mfma = [&](f32x16 (&X)[NB], const char* tb, uint32_t w) {
+    if (w == kFull) {
+      mfma_tile_pad<E, DIM, NB>(X, tb, bf, a_off);
+    } else {
+      f32x16 c0;
+      tile_init(c0, w, h);
+      mfma_tile_c<E, DIM, NB>(X, tb, bf, a_off, c0);
+    }
+  };
   BlockState st[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) state_init(st[b], 0);
+  int cur = 0;                                   // stage of entry e
+  // schedule words are read one step ahead, so no LDS round trip stands
+  // between a step's start and its first load or MFMA
+  const int last = S > 0 ? S - 1 : 0;
+  int n_meta = s_meta[0], n_unit = s_unit[0];
+  uint32_t n_w0 = s_w0[0], n_w1 = s_w1[0];
+  int l_meta = s_meta[min(NST - 1, last)], l_unit = s_unit[min(NST - 1, last)];
   for (int e = 0; e < S; ++e) {
-    const int meta = __builtin_amdgcn_readfirstlane(s_meta[e]);
-    const uint32_t word0 = __builtin_amdgcn_readfirstlane(s_w0[e]);
-    const uint32_t word1 = __builtin_amdgcn_readfirstlane(s_w1[e]);
+    const int meta = __builtin_amdgcn_readfirstlane(n_meta);
+    const int unit = __builtin_amdgcn_readfirstlane(n_unit);
+    const uint32_t word0 = __builtin_amdgcn_readfirstlane(n_w0);
+    const uint32_t word1 = __builtin_amdgcn_readfirstlane(n_w1);
+    const int ld_meta = __builtin_amdgcn_readfirstlane(l_meta);
+    const int ld_unit = __builtin_amdgcn_readfirstlane(l_unit);
+    {
+      const int en = min(e + 1, last), el = min(e + NST, last);
+      n_meta = s_meta[en];
+      n_unit = s_unit[en];
+      n_w0 = s_w0[en];
+      n_w1 = s_w1[en];
+      l_meta = s_meta[el];
+      l_unit = s_unit[el];
+    }
     const int t = meta & 0xffffff;
     const bool two = (meta >> 24) & 1, ustart = (meta >> 25) & 1, uend = (meta >> 26) & 1;
     const bool has = (meta >> 27) & 1;
-    // the next entry's tiles are loaded now (the last entry reloads its own)
-    const bool nxt = e + 1 < S;
-    gload(nxt ? e + 1 : e);
+    // entry e+NST-1 goes to the stage entry e-1 used (every wave passed the
+    // barrier after reading it); past the end the last entry is reloaded
+    const int st_ld = cur == 0 ? NST - 1 : cur - 1;
+    gload(ld_meta, ld_unit, st_ld);
     if (ustart) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) state_init(st[b], t);
     }
     if (active && has) {
       const char* buf = lds + cur * kSTBytes;
-      mfma_tile_pad<E, DIM, NB>(X, buf, bf, a_off);
-      if (word0 != kFull) tiles_mask<NB>(X, word0, h);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t);
+      tile_mfma(Xa, buf, word0);
       if (two) {
-        mfma_tile_pad<E, DIM, NB>(X, buf + PD::kTileBytes, bf, a_off);
-        if (word1 != kFull) tiles_mask<NB>(X, word1, h);
+        tile_mfma(Xb, buf + PD::kTileBytes, word1);
+        if constexpr (KEEP) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], X[b], t + 1);
+          for (int b = 0; b < NB; ++b) state_fold_pair(st[b], Xa[b], Xb[b], t);
+        } else {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            st[b].run_max = __builtin_fmaxf(st[b].run_max,
+                                            __builtin_fmaxf(max16(Xa[b]), max16(Xb[b])));
+        }
+      } else {
+        if constexpr (KEEP) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], Xa[b], t);
+        } else {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) st[b].run_max = __builtin_fmaxf(st[b].run_max, max16(Xa[b]));
+        }
       }
     }
-    if (nxt) lstore(lds + (cur ^ 1) * kSTBytes);
+    // entry e+1's rows (loaded one step ago) must be in LDS before the barrier
+    wait_stage();
     if (uend && active) {
       // flush this unit
-      const int unit = __builtin_amdgcn_readfirstlane(s_unit[e]);
       const int cd = unit >> 8, cc = unit & 0xff;
       float M[NB];
       int J[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) state_resolve(st[b], h, M[b], J[b]);
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (KEEP) {
+          state_resolve(st[b], h, M[b], J[b]);
+        } else {
+          M[b] = st[b].run_max;
+          J[b] = 0;
+        }
+      }
       float Mv;
       int Jv;
       combine_halves<NB>(M, J, lane, Mv, Jv);
@@ -349,7 +440,7 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
         if (writer) {
           const int64_t idx = ((int64_t)cc * a.n_docs + cd) * a.n_cg * SPW + part_lane;
           a.part_M[idx] = has ? Mv : -__builtin_inff();
-          a.part_J[idx] = has ? Jv : -1;
+          if constexpr (KEEP) a.part_J[idx] = has ? Jv : -1;
         }
       } else {
         const bool empty = !has;          // single chunk: no tile means no valid token
@@ -358,13 +449,20 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
         if (slot_ok && writer) {
           const int64_t pair = score_base + cd;
           if (seg_last) a.scores[pair] = empty ? kEmptyDocScore : sc;
-          if (a.argmax) a.argmax[pair * a.Lq + slot_i] = (slot_tok && !empty) ? Jv : -1;
+          if constexpr (KEEP) a.argmax[pair * a.Lq + slot_i] = (slot_tok && !empty) ? Jv : -1;
         }
       }
     }
-    __syncthreads();
-    cur ^= 1;
+    // A plain s_barrier: the tile data needs no memory fence (each wave has
+    // waited for its own loads above), and __syncthreads() would also wait
+    // for the loads still in flight for the entry after next.
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    cur = cur == NST - 1 ? 0 : cur + 1;
   }
+  // drain this wave's last (redundant) loads before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // ---------------------------------------------------------------------------
@@ -495,52 +593,82 @@ __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // combine: one wave per output (query, doc) / pair
 // ---------------------------------------------------------------------------
+// One workgroup per output: 64 query-token lanes x 4 chunk groups; each
+// thread merges every 4th chunk with independent loads, then group 0 merges
+// the 4 partials (the larger max wins, ties to the lower index: the result
+// does not depend on the merge order) and sums over the valid tokens.
 __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t out = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float sM[4][64];
+  __shared__ int sJ[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 6;
   const bool ap = a.layout == kAllPairs;
   const int64_t n_out = ap ? a.Nq * a.n_docs : a.n_docs;
-  if (out >= n_out) return;
-  const int64_t q = ap ? out / a.n_docs : out / a.K;
-  const int64_t e = ap ? out - q * a.n_docs : out;
-  const bool empty = a.ntiles ? a.ntiles[e] == 0 : a.Ld == 0;
-  float total = 0.0f;
-  for (int64_t i0 = 0; i0 < a.Lq; i0 += 64) {
-    const int64_t i = i0 + lane;
-    const bool ok = i < a.Lq;
-    int64_t cg, slot;
-    if (ap) {
-      if (a.qpw > 0) {
-        cg = q / a.qpw;
-        slot = (q - cg * a.qpw) * a.Lq + i;
+  for (int64_t out = blockIdx.x; out < n_out; out += gridDim.x) {
+    const int64_t q = ap ? out / a.n_docs : out / a.K;
+    const int64_t e = ap ? out - q * a.n_docs : out;
+    const bool empty = a.ntiles ? a.ntiles[e] == 0 : a.Ld == 0;
+    float total = 0.0f;
+    for (int64_t i0 = 0; i0 < a.Lq; i0 += 64) {
+      const int64_t i = i0 + lane;
+      const bool ok = i < a.Lq;
+      int64_t cg, slot;
+      if (ap) {
+        if (a.qpw > 0) {
+          cg = q / a.qpw;
+          slot = (q - cg * a.qpw) * a.Lq + i;
+        } else {
+          const int64_t s = q * a.Lq + i;
+          cg = s / a.SPW;
+          slot = s - cg * a.SPW;
+        }
       } else {
-        const int64_t s = q * a.Lq + i;
-        cg = s / a.SPW;
-        slot = s - cg * a.SPW;
+        cg = i / a.SPW;
+        slot = i - cg * a.SPW;
       }
-    } else {
-      cg = i / a.SPW;
-      slot = i - cg * a.SPW;
-    }
-    float M = -__builtin_inff();
-    int J = -1;
-    if (ok) {
-      for (int64_t c = 0; c < a.nchunks; ++c) {
-        const int64_t idx = ((c * a.n_docs + e) * a.n_cg + cg) * a.SPW + slot;
-        merge_mj(M, J, a.part_M[idx], a.part_J[idx]);
+      float M = -__builtin_inff();
+      int J = -1;
+      if (ok) {
+        const int64_t stride = a.n_docs * a.n_cg * a.SPW;      // between chunks
+        const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
+        constexpr int U = 4;
+        for (int64_t c0 = grp; c0 < a.nchunks; c0 += 4 * U) {
+          float mm[U];
+          int jj[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + 4 * u;
+            mm[u] = -__builtin_inff();
+            jj[u] = -1;
+            if (c < a.nchunks) {
+              mm[u] = a.part_M[c * stride + base];
+              // without an argmax output the indices are not kept
+              jj[u] = a.argmax ? a.part_J[c * stride + base] : 0;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) merge_mj(M, J, mm[u], jj[u]);
+        }
       }
+      sM[grp][lane] = M;
+      sJ[grp][lane] = J;
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int g2 = 1; g2 < 4; ++g2) merge_mj(M, J, sM[g2][lane], sJ[g2][lane]);
+        const bool tok = ok && (!a.q_mask || a.q_mask[q * a.Lq + i]);
+        total += wave_sum(tok ? M : 0.0f);
+        if (ok && a.argmax) a.argmax[out * a.Lq + i] = (tok && !empty) ? J : -1;
+      }
+      __syncthreads();
     }
-    const bool tok = ok && (!a.q_mask || a.q_mask[q * a.Lq + i]);
-    total += wave_sum(tok ? M : 0.0f);
-    if (ok && a.argmax) a.argmax[out * a.Lq + i] = (tok && !empty) ? J : -1;
+    if (tid == 0) a.scores[out] = empty ? kEmptyDocScore : total;
   }
-  if (lane == 0) a.scores[out] = empty ? kEmptyDocScore : total;
 }
 
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <Elem E, int DIM, int NB, bool MASK>
+template <Elem E, int DIM, int NB, bool MASK, bool KEEP>
 static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
   hipEvent_t ev0, ev1;
@@ -554,11 +682,11 @@ static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t 
     constexpr int lds = ap_lds_bytes<E, DIM>();
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&allpairs_fwd_kernel<E, DIM, NB, MASK>),
+          reinterpret_cast<const void*>(&allpairs_fwd_kernel<E, DIM, NB, MASK, KEEP>),
           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((allpairs_fwd_kernel<E, DIM, NB, MASK>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((allpairs_fwd_kernel<E, DIM, NB, MASK, KEEP>), dim3((unsigned)grid),
                        dim3(kApThreads), lds, s, a);
   } else {
     constexpr int W = pr_waves<E, DIM>();
@@ -573,7 +701,13 @@ static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t 
 
 template <Elem E, int DIM, int NB>
 static hipError_t launch_main(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
-  return a.bits ? launch_main_m<E, DIM, NB, true>(p, a, s) : launch_main_m<E, DIM, NB, false>(p, a, s);
+  // the pairs kernel always tracks the argmax (it is bandwidth-bound)
+  const bool keep = a.argmax != nullptr || p.layout != kAllPairs;
+  if (a.bits)
+    return keep ? launch_main_m<E, DIM, NB, true, true>(p, a, s)
+                : launch_main_m<E, DIM, NB, true, false>(p, a, s);
+  return keep ? launch_main_m<E, DIM, NB, false, true>(p, a, s)
+              : launch_main_m<E, DIM, NB, false, false>(p, a, s);
 }
 
 template <Elem E>
@@ -650,7 +784,8 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
   if (e != hipSuccess) return e;
   if (p.partial) {
     const int64_t n_out = p.layout == kAllPairs ? p.Nq * p.n_docs : p.n_docs;
-    hipLaunchKernelGGL(combine_fwd_kernel, dim3((unsigned)cdiv(n_out, 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(combine_fwd_kernel, dim3((unsigned)(n_out < 65536 ? n_out : 65536)), dim3(256),
+                       0, s, a);
     e = hipGetLastError();
   }
   return e;

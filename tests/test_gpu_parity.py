@@ -14,7 +14,7 @@ import torch
 import oracle
 from maxsim_scoring_02_amd import workloads as wl
 from maxsim_scoring_02_amd.workloads import Workload
-from parity import full_check, gpu_backward, gpu_forward, say
+from parity import ORACLE_FWD, check_scores, full_check, gpu_backward, gpu_forward, say
 
 pytestmark = pytest.mark.gpu
 
@@ -171,6 +171,27 @@ def test_hub_rows_collect_most_hits():
     full_check(w)
     s, a = gpu_forward(w)
     assert np.mean(a[:, 0] == 7) > 0.9 and np.all(a[:, 1] != 50)
+
+
+def test_scores_without_argmax_output():
+    """With no argmax buffer the forward keeps running maxima only (all-pairs)
+    or drops the indices of split partials; the scores must be bitwise those
+    of the argmax-keeping forward, in direct, split and masked modes."""
+    rng = np.random.default_rng(1500)
+    Q = _rand_tokens(rng, (9, 32, 128))
+    D = _rand_tokens(rng, (11, 2200, 128))
+    dm = np.arange(2200)[None] < rng.integers(1, 2201, 11)[:, None]
+    dm[4] = False
+    cases = [wl.inbatch_text(B=20, Nd=30),
+             _custom("noarg-split", "allpairs", "f16", Q, D, None, dm),
+             _custom("noarg-full", "allpairs", "bf16", Q, D[:, :300], None, None),
+             _custom("noarg-pair", "pairwise", "bf16", Q, D[:9], None, dm[:9])]
+    for w in cases:
+        s0, a0 = gpu_forward(w, keep_argmax=False)
+        s1, _ = gpu_forward(w, keep_argmax=True)
+        assert a0 is None
+        assert np.array_equal(s0, s1), w.name
+        check_scores(s0, ORACLE_FWD[w.layout](*w.numpy_inputs()))
 
 
 def test_arbitrary_masks_and_degenerate_rows():
