@@ -125,19 +125,41 @@ constexpr int ap_lds_bytes() {
   return ap_stages<E, DIM>() * kSub * Pad<E, DIM>::kTileBytes;
 }
 
+// The tile's A chunks are read from LDS up to kWin ahead of the MFMAs that
+// use them, so an MFMA waits on LDS latency only at the start of a tile.  The
+// order (kWin reads, then per chunk its MFMAs and the next read) is pinned for
+// the scheduler, which otherwise interleaves one read per MFMA pair.
+template <Elem E, int DIM, int NB>
+__device__ __forceinline__ void mfma_tile_run(f32x16 (&acc)[NB], const char* buf,
+                                              const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
+                                              int a_off) {
+  using G = Geo<E, DIM>;
+  constexpr int KS = G::kKSteps;
+  constexpr int kWin = KS < 8 ? KS : 8;
+  constexpr int kMfmaPerChunk = NB * (E == Elem::F32 ? 4 : 1);
+  u32x4 av[KS];
+#pragma unroll
+  for (int m = 0; m < kWin; ++m) av[m] = ld_lds_16(buf, a_off + m * 32);
+  __builtin_amdgcn_sched_group_barrier(0x100, kWin, 0);
+#pragma unroll
+  for (int m = 0; m < KS; ++m) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mfma_chunk<E>(acc[b], av[m], bf[b][m]);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk, 0);
+    if (m + kWin < KS) {
+      av[m + kWin] = ld_lds_16(buf, a_off + (m + kWin) * 32);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+}
+
 template <Elem E, int DIM, int NB>
 __device__ __forceinline__ void mfma_tile_pad(f32x16 (&acc)[NB], const char* buf,
                                               const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
                                               int a_off) {
-  using G = Geo<E, DIM>;
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-#pragma unroll
-  for (int m = 0; m < G::kKSteps; ++m) {
-    const u32x4 av = ld_lds_16(buf, a_off + m * 32);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) mfma_chunk<E>(acc[b], av, bf[b][m]);
-  }
+  mfma_tile_run<E, DIM, NB>(acc, buf, bf, a_off);
 }
 
 // acc = C + A * B over one tile, with C the tile's initial value (zero, or
@@ -146,16 +168,52 @@ template <Elem E, int DIM, int NB>
 __device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
                                             const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
                                             int a_off, const f32x16& c0) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = c0;
+  mfma_tile_run<E, DIM, NB>(acc, buf, bf, a_off);
+}
+
+// Both tiles of a super-tile at once: four independent accumulator chains
+// (two tiles x NB), so an MFMA never waits on the result of the one issued
+// just before it.  Chunks of both tiles are read kWin steps ahead.  With
+// ZERO the chains start from zero, else from ca / cb (the masked-row init).
+template <Elem E, int DIM, int NB, bool ZERO>
+__device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB],
+                                              const char* bufa, const char* bufb,
+                                              const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
+                                              int a_off, const f32x16& ca, const f32x16& cb) {
   using G = Geo<E, DIM>;
+  constexpr int KS = G::kKSteps;
+  constexpr int kWin = E == Elem::F32 ? 2 : (KS < 4 ? KS : 4);
+  constexpr int kMfmaPerChunk = NB * (E == Elem::F32 ? 4 : 1);
 #pragma unroll
-  for (int m = 0; m < G::kKSteps; ++m) {
-    const u32x4 av = ld_lds_16(buf, a_off + m * 32);
+  for (int b = 0; b < NB; ++b) {
+    if constexpr (ZERO) {
+      xa[b] = f32x16{};
+      xb[b] = f32x16{};
+    } else {
+      xa[b] = ca;
+      xb[b] = cb;
+    }
+  }
+  u32x4 aa[KS], ab[KS];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (m == 0) {
-        acc[b] = c0;
-      }
-      mfma_chunk<E>(acc[b], av, bf[b][m]);
+  for (int m = 0; m < kWin; ++m) {
+    aa[m] = ld_lds_16(bufa, a_off + m * 32);
+    ab[m] = ld_lds_16(bufb, a_off + m * 32);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWin, 0);
+#pragma unroll
+  for (int m = 0; m < KS; ++m) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mfma_chunk<E>(xa[b], aa[m], bf[b][m]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) mfma_chunk<E>(xb[b], ab[m], bf[b][m]);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerChunk, 0);
+    if (m + kWin < KS) {
+      aa[m + kWin] = ld_lds_16(bufa, a_off + (m + kWin) * 32);
+      ab[m + kWin] = ld_lds_16(bufb, a_off + (m + kWin) * 32);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
 }
@@ -395,9 +453,16 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     }
     if (active && has) {
       const char* buf = lds + cur * kSTBytes;
-      tile_mfma(Xa, buf, word0);
       if (two) {
-        tile_mfma(Xb, buf + PD::kTileBytes, word1);
+        if (word0 == kFull && word1 == kFull) {
+          mfma_pair_run<E, DIM, NB, true>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, Xa[0],
+                                          Xb[0]);
+        } else {
+          f32x16 ca, cb;                 // a full word gives an all-zero init
+          tile_init(ca, word0, h);
+          tile_init(cb, word1, h);
+          mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb);
+        }
         if constexpr (KEEP) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) state_fold_pair(st[b], Xa[b], Xb[b], t);
@@ -408,6 +473,7 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
                                             __builtin_fmaxf(max16(Xa[b]), max16(Xb[b])));
         }
       } else {
+        tile_mfma(Xa, buf, word0);
         if constexpr (KEEP) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], Xa[b], t);
@@ -665,6 +731,80 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Few chunks: one wave per output (two, one per 32-lane half, when Lq <= 32).
+// A lane owns a query token and merges its chunks in order with independent
+// loads; no LDS and no barrier.  Same merge rule as above.
+constexpr int kCombineWaveMaxChunks = 16;
+
+__global__ __launch_bounds__(256) void combine_fwd_wave_kernel(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const bool half = a.Lq <= 32;
+  const int per_wave = half ? 2 : 1;
+  const int gs = half ? 32 : 64;                 // lanes per output
+  const int sub = half ? lane >> 5 : 0;
+  const int li = half ? (lane & 31) : lane;
+  const bool ap = a.layout == kAllPairs;
+  const int64_t n_out = ap ? a.Nq * a.n_docs : a.n_docs;
+  const int64_t n_waves = (n_out + per_wave - 1) / per_wave;
+  const int64_t stride = a.n_docs * a.n_cg * a.SPW;      // between chunks
+  for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < n_waves;
+       w += (int64_t)gridDim.x * 4) {
+    const int64_t out_raw = w * per_wave + sub;
+    const bool out_ok = out_raw < n_out;
+    const int64_t out = out_ok ? out_raw : n_out - 1;    // a clamped lane never stores
+    const int64_t q = ap ? out / a.n_docs : out / a.K;
+    const int64_t e = ap ? out - q * a.n_docs : out;
+    const bool empty = a.ntiles ? a.ntiles[e] == 0 : a.Ld == 0;
+    float total = 0.0f;
+    for (int64_t i0 = 0; i0 < a.Lq; i0 += gs) {
+      const int64_t i = i0 + li;
+      const bool ok = i < a.Lq;
+      int64_t cg, slot;
+      if (ap) {
+        if (a.qpw > 0) {
+          cg = q / a.qpw;
+          slot = (q - cg * a.qpw) * a.Lq + i;
+        } else {
+          const int64_t s2 = q * a.Lq + i;
+          cg = s2 / a.SPW;
+          slot = s2 - cg * a.SPW;
+        }
+      } else {
+        cg = i / a.SPW;
+        slot = i - cg * a.SPW;
+      }
+      float M = -__builtin_inff();
+      int J = -1;
+      if (ok) {
+        const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
+        constexpr int U = 4;
+        for (int64_t c0 = 0; c0 < a.nchunks; c0 += U) {
+          float mm[U];
+          int jj[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u;
+            mm[u] = -__builtin_inff();
+            jj[u] = -1;
+            if (c < a.nchunks) {
+              mm[u] = a.part_M[c * stride + base];
+              jj[u] = a.argmax ? a.part_J[c * stride + base] : 0;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) merge_mj(M, J, mm[u], jj[u]);
+        }
+      }
+      const bool tok = ok && (!a.q_mask || a.q_mask[q * a.Lq + i]);
+      float v = tok ? M : 0.0f;
+      for (int k = gs >> 1; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+      total += v;
+      if (out_ok && ok && a.argmax) a.argmax[out * a.Lq + i] = (tok && !empty) ? J : -1;
+    }
+    if (out_ok && li == 0) a.scores[out] = empty ? kEmptyDocScore : total;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -784,8 +924,14 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
   if (e != hipSuccess) return e;
   if (p.partial) {
     const int64_t n_out = p.layout == kAllPairs ? p.Nq * p.n_docs : p.n_docs;
-    hipLaunchKernelGGL(combine_fwd_kernel, dim3((unsigned)(n_out < 65536 ? n_out : 65536)), dim3(256),
-                       0, s, a);
+    if (p.nchunks <= kCombineWaveMaxChunks) {
+      const int64_t blocks = cdiv(cdiv(n_out, p.Lq <= 32 ? 2 : 1), 4);
+      hipLaunchKernelGGL(combine_fwd_wave_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                         dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(combine_fwd_kernel, dim3((unsigned)(n_out < 65536 ? n_out : 65536)),
+                         dim3(256), 0, s, a);
+    }
     e = hipGetLastError();
   }
   return e;
