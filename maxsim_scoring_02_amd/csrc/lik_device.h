@@ -270,6 +270,18 @@ __device__ __forceinline__ void merge_mj(float& M, int& J, float M2, int J2) {
   J = take ? J2 : J;
 }
 
+// The value of lane (l ^ 32), by one swap of the wave's halves (a VALU
+// operation, no LDS round trip): the swap returns the upper half of its first
+// operand's lanes moved down in its second result and the lower half moved up
+// in its first.
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return lane < 32 ? r[1] : r[0];
+}
+__device__ __forceinline__ float xor32_f32(float x, int lane) {
+  return __uint_as_float(xor32_u32(__float_as_uint(x), lane));
+}
+
 // After the two row halves of a column are merged, lane L of the wave holds
 // the result of slot L (NB == 2: block L/32, column L%32) or slot L%32
 // (NB == 1, both halves hold it).
@@ -282,15 +294,15 @@ __device__ __forceinline__ void combine_halves(const float (&M)[NB], const int (
     int own_j = lo ? J[0] : J[1];
     float give_m = lo ? M[1] : M[0];
     int give_j = lo ? J[1] : J[0];
-    float oth_m = __shfl_xor(give_m, 32);
-    int oth_j = __shfl_xor(give_j, 32);
+    float oth_m = xor32_f32(give_m, lane);
+    int oth_j = (int)xor32_u32((uint32_t)give_j, lane);
     merge_mj(own_m, own_j, oth_m, oth_j);
     Mout = own_m;
     Jout = own_j;
   } else {
     float own_m = M[0];
     int own_j = J[0];
-    merge_mj(own_m, own_j, __shfl_xor(own_m, 32), __shfl_xor(own_j, 32));
+    merge_mj(own_m, own_j, xor32_f32(own_m, lane), (int)xor32_u32((uint32_t)own_j, lane));
     Mout = own_m;
     Jout = own_j;
   }

@@ -218,6 +218,15 @@ __device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB]
   }
 }
 
+// Workgroup barrier that waits for this wave's LDS operations only:
+// __syncthreads() would also wait for every global load still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt left at their maxima
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // KEEP: the caller wants the argmax; without it only running maxima are kept.
 template <Elem E, int DIM, int NB, bool MASK, bool KEEP>
 __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
@@ -257,19 +266,57 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   // hot loop below holds no cursor arithmetic and no global index loads.
   const int nchunks = (int)a.nchunks, tpc = (int)a.tpc;
   const int64_t n_units = a.n_docs * a.nchunks;
-  const int64_t u_begin = (int64_t)g * a.upw;
-  const int n_my = (int)(min(u_begin + a.upw, n_units) - u_begin);
+  // Units are numbered chunk-major (u = chunk * n_docs + document) and dealt
+  // out strided (unit k of this workgroup is g + k * n_groups), so every
+  // workgroup gets about as many units of each chunk index: a mix of long,
+  // partial and empty chunks.
+  const int64_t n_grp = a.n_groups;
+  const int n_my = (int)min((int64_t)a.upw, (n_units - g + n_grp - 1) / n_grp);
+  auto unit_dc = [&](int k, int& d, int& c) {
+    const int64_t u = g + (int64_t)k * n_grp;
+    c = (int)(u / a.n_docs);
+    d = (int)(u - (int64_t)c * a.n_docs);
+  };
   const int Ld = (int)a.Ld;
   __shared__ int s_meta[kApMaxST];     // t | two << 24 | start << 25 | end << 26 | has << 27
   __shared__ int s_unit[kApMaxST];     // d << 8 | chunk
   __shared__ uint32_t s_w0[kApMaxST], s_w1[kApMaxST];
   __shared__ int s_uoff[kApMaxDocs + 1], s_ut0[kApMaxDocs], s_ut1[kApMaxDocs];
+
+  // Set-up in two rounds of global reads.  First the units' tile counts and
+  // every validity word of the schedule, all issued before any is used
+  // (words past a document's last valid tile are zero, so they are read
+  // before the counts are known, bounded only by the document's word count).
+  // Schedule entry x = (unit x / 32, pair j = x % 32), kSetupIt per thread.
+  int unit_nt = 0;                      // wave 0, lane k: tile count of unit k's document
+  if (MASK && wave == 0 && lane < n_my) {
+    int d, c;
+    unit_dc(lane, d, c);
+    unit_nt = a.ntiles[d];
+  }
+  constexpr int kSetupIt = kApMaxDocs * 32 / kApThreads;
+  uint32_t pw0[kSetupIt], pw1[kSetupIt];
+#pragma unroll
+  for (int it = 0; it < kSetupIt; ++it) {
+    const int x = tid + it * kApThreads;
+    pw0[it] = pw1[it] = 0u;
+    if (MASK && x < n_my * 32) {
+      const int k = x >> 5, j = x & 31;
+      int d, c;
+      unit_dc(k, d, c);
+      const int t = c * tpc + 2 * j;
+      const uint32_t* wd = a.bits + (int64_t)d * a.nwords;
+      if (2 * j < tpc && t < a.nwords) pw0[it] = wd[t];
+      if (2 * j + 1 < tpc && t + 1 < a.nwords) pw1[it] = wd[t + 1];
+    }
+  }
+
   if (wave == 0) {
     int nst = 0, t0 = 0, t1 = 0;
     if (lane < n_my) {
-      const int64_t u = u_begin + lane;
-      const int d = (int)(u / nchunks), c = (int)(u - (int64_t)d * nchunks);
-      const int nt = MASK ? a.ntiles[d] : (int)a.ntiles_max;
+      int d, c;
+      unit_dc(lane, d, c);
+      const int nt = MASK ? unit_nt : (int)a.ntiles_max;
       t0 = c * tpc;
       t1 = min(t0 + tpc, nt);
       if (t1 < t0) t1 = t0;
@@ -288,53 +335,31 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     }
     if (lane == 63) s_uoff[kApMaxDocs] = incl;
   }
-  __syncthreads();
-  for (int x = tid; x < n_my * 32; x += kApThreads) {
-    const int k = x >> 5, j = x & 31;
-    const int t0 = s_ut0[k], t1 = s_ut1[k], off = s_uoff[k];
-    const int nst = t1 > t0 ? (t1 - t0 + 1) / 2 : 1;
-    if (j < nst) {
-      const int64_t u = u_begin + k;
-      const int d = (int)(u / nchunks), c = (int)(u - (int64_t)d * nchunks);
-      const int t = t0 + 2 * j;
-      const bool has = t < t1, two = t + 1 < t1;
-      uint32_t w0 = 0u, w1 = 0u;
-      if (has) w0 = MASK ? a.bits[(int64_t)d * a.nwords + t] : tile_word(nullptr, t, Ld);
-      if (two) w1 = MASK ? a.bits[(int64_t)d * a.nwords + t + 1] : tile_word(nullptr, t + 1, Ld);
-      s_w0[off + j] = w0;
-      s_w1[off + j] = w1;
-      s_meta[off + j] = t | ((int)two << 24) | ((int)(j == 0) << 25) | ((int)(j == nst - 1) << 26) |
-                        ((int)has << 27);
-      s_unit[off + j] = (d << 8) | c;
-    }
-  }
-
-  // query fragments of this wave's slots (B operand), kept for all units
-  u32x4 bf[NB][G::kKSteps];
-  {
-    int64_t rows[NB];
-    bool ok[NB];
+  lds_barrier();
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      int64_t q, i;
-      ok[b] = active && slot_qi(gw, b * 32 + r, SPW, a.qpw, a.Nq, a.Lq, q, i);
-      rows[b] = ok[b] ? q * a.Lq + i : 0;
+  for (int it = 0; it < kSetupIt; ++it) {
+    const int x = tid + it * kApThreads;
+    if (x < n_my * 32) {
+      const int k = x >> 5, j = x & 31;
+      const int t0 = s_ut0[k], t1 = s_ut1[k], off = s_uoff[k];
+      const int nst = t1 > t0 ? (t1 - t0 + 1) / 2 : 1;
+      if (j < nst) {
+        int d, c;
+        unit_dc(k, d, c);
+        const int t = t0 + 2 * j;
+        const bool has = t < t1, two = t + 1 < t1;
+        uint32_t w0 = 0u, w1 = 0u;
+        if (has) w0 = MASK ? pw0[it] : tile_word(nullptr, t, Ld);
+        if (two) w1 = MASK ? pw1[it] : tile_word(nullptr, t + 1, Ld);
+        s_w0[off + j] = w0;
+        s_w1[off + j] = w1;
+        s_meta[off + j] = t | ((int)two << 24) | ((int)(j == 0) << 25) | ((int)(j == nst - 1) << 26) |
+                          ((int)has << 27);
+        s_unit[off + j] = (d << 8) | c;
+      }
     }
-    load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
   }
-  // this lane's output slot, fixed for the whole kernel
-  const int L = NB == 2 ? lane : (lane & 31);
-  const bool writer = NB == 2 || lane < 32;
-  int64_t slot_q = 0, slot_i = 0;
-  const bool slot_ok = active && slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, slot_q, slot_i);
-  const bool slot_tok = slot_ok && (!a.q_mask || a.q_mask[slot_q * a.Lq + slot_i]);
-  const int seg_start = a.qpw > 0 ? (int)((L / a.Lq) * a.Lq) : 0;
-  const bool seg_last = slot_ok && slot_i == a.Lq - 1;
-  // queries of 32 tokens two to a wave: their sums are lane-aligned halves
-  const bool fast_sum = a.qpw > 0 && a.Lq == 32;
-  const int64_t score_base = slot_q * a.n_docs;
-  const int64_t part_lane = (int64_t)gw * SPW + L;
-  __syncthreads();
+  lds_barrier();
   const int S = s_uoff[kApMaxDocs];
 
   // Super-tiles are copied global -> LDS directly (no registers): the padded
@@ -391,14 +416,37 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     }
   };
 
+  // prologue: the first entries' tiles, the query fragments and the query
+  // mask are all requested before any is waited for
   if (S > 0) gload(__builtin_amdgcn_readfirstlane(s_meta[0]), __builtin_amdgcn_readfirstlane(s_unit[0]), 0);
-  if (NST == 3 && S > 1) {
+  if (NST == 3 && S > 1)
     gload(__builtin_amdgcn_readfirstlane(s_meta[1]), __builtin_amdgcn_readfirstlane(s_unit[1]), 1);
-    wait_stage();
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  u32x4 bf[NB][G::kKSteps];
+  {
+    int64_t rows[NB];
+    bool ok[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      int64_t q, i;
+      ok[b] = active && slot_qi(gw, b * 32 + r, SPW, a.qpw, a.Nq, a.Lq, q, i);
+      rows[b] = ok[b] ? q * a.Lq + i : 0;
+    }
+    load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
   }
-  __syncthreads();
+  // this lane's output slot, fixed for the whole kernel
+  const int L = NB == 2 ? lane : (lane & 31);
+  const bool writer = NB == 2 || lane < 32;
+  int64_t slot_q = 0, slot_i = 0;
+  const bool slot_ok = active && slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, slot_q, slot_i);
+  const bool slot_tok = slot_ok && (!a.q_mask || a.q_mask[slot_q * a.Lq + slot_i]);
+  const int seg_start = a.qpw > 0 ? (int)((L / a.Lq) * a.Lq) : 0;
+  const bool seg_last = slot_ok && slot_i == a.Lq - 1;
+  // queries of 32 tokens two to a wave: their sums are lane-aligned halves
+  const bool fast_sum = a.qpw > 0 && a.Lq == 32;
+  const int64_t score_base = slot_q * a.n_docs;
+  const int64_t part_lane = (int64_t)gw * SPW + L;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
 
   const int a_off = r * PD::kStride + h * 16;
   f32x16 Xa[NB], Xb[NB];
