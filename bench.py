@@ -5,8 +5,11 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 that is already resident in HBM: the forward (scores + int32 argmax) and, for
 training workloads, the backward (grad_Q and grad_D in float32).  W untimed
-steps, then exactly K timed steps between two device synchronisations; rank 0
-prints one JSON line.
+steps, then exactly K timed steps between two device synchronisations, with
+one HIP event at each end of them and none in between; rank 0 prints one JSON
+line.  Two untimed passes follow: K steps with events between forward and
+backward (`config.fwd_ms`, `config.bwd_ms`) and K forwards with the
+library's events around its main kernel (`roofline.kernel_ms`).
 
 Default workload: ColBERT-text in-batch contrastive fwd+bwd -- 256 queries x
 32 tokens against 256 documents padded to 300 tokens (true lengths uniform in
@@ -363,12 +366,24 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
         if backward:
             op.bwd()
     E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [(E(), E(), E()) for _ in range(steps)]
-    kev = HipEvents(op.L, steps)          # around the main forward kernel
+    # Timed region: K whole steps with one event at each end and nothing
+    # between them (every event between kernels adds a marker packet and
+    # idles the GPU for a few microseconds).
+    s0, s1 = E(), E()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k, (e0, e1, e2) in enumerate(ev):
-        op.L.lik_set_profile_events(*kev.ev[k])
+    s0.record()
+    for _ in range(steps):
+        op.fwd()
+        if backward:
+            op.bwd()
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = s0.elapsed_time(s1) / steps
+    # Breakdown pass, outside the timed region: forward and backward apart.
+    ev = [(E(), E(), E()) for _ in range(steps)]
+    for e0, e1, e2 in ev:
         e0.record()
         op.fwd()
         e1.record()
@@ -376,14 +391,18 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
             op.bwd()
         e2.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    op.L.lik_set_profile_events(None, None)
     fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
     bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
+    # Kernel pass: HIP events recorded by the library around the main forward
+    # kernel on its own stream (the roofline's duration).
+    kev = HipEvents(op.L, steps)
+    for k in range(steps):
+        op.L.lik_set_profile_events(*kev.ev[k])
+        op.fwd()
+    op.L.lik_set_profile_events(None, None)
+    torch.cuda.synchronize()
     kern_ms = [kev.elapsed_ms(k) for k in range(steps)]
     kev.close()
-    span_ms = ev[0][0].elapsed_time(ev[-1][2])
-    ms_step = span_ms / steps
     t_fwd = float(np.mean(fwd_ms))
     t_bwd = float(np.mean(bwd_ms)) if backward else 0.0
     t_kern = float(np.mean(kern_ms))
