@@ -24,29 +24,38 @@ namespace lik {
 constexpr float kEmptyDocScore = -1e9f;
 
 // ---------------------------------------------------------------------------
-// mask prep: one wave per document
+// mask prep: one wave per document.  A wave reads 64 consecutive mask bytes
+// (one per lane, coalesced) and a ballot of "byte != 0" is directly two tile
+// words; U blocks are read before any is used.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mask_prep_kernel(const uint8_t* __restrict__ d_mask,
                                                         int64_t n_docs, int64_t Ld, int64_t nwords,
                                                         uint32_t* __restrict__ bits,
                                                         int32_t* __restrict__ ntiles) {
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int64_t d = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (d >= n_docs) return;
+  if (d >= n_docs) return;                        // whole wave
   const uint8_t* m = d_mask + d * Ld;
-  int last = -1;
-  for (int64_t w = lane; w < nwords; w += 64) {
-    uint32_t word = 0;
-    const int64_t j0 = w * 32;
-    for (int b = 0; b < 32; ++b) {
-      const int64_t j = j0 + b;
-      if (j < Ld && m[j]) word |= 1u << b;
-    }
-    bits[d * nwords + w] = word;
-    if (word) last = (int)w;
-  }
+  uint32_t* out = bits + d * nwords;
+  const int64_t nblk = (Ld + 63) / 64;
+  int last = -1;                                  // last word with a valid row (wave-uniform)
+  for (int64_t b0 = 0; b0 < nblk; b0 += U) {
+    uint8_t v[U];
 #pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) last = max(last, __shfl_xor(last, k));
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = (b0 + u) * 64 + lane;
+      v[u] = j < Ld ? m[j] : (uint8_t)0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t bal = __ballot(v[u] != 0);
+      const int64_t w = 2 * (b0 + u);
+      if (lane < 2 && w + lane < nwords) out[w + lane] = (uint32_t)(bal >> (32 * lane));
+      if (bal >> 32) last = (int)w + 1;
+      else if (bal) last = (int)w;
+    }
+  }
   if (lane == 0) ntiles[d] = last + 1;
 }
 
