@@ -1,0 +1,131 @@
+"""Host-side invariants of the launch plans (lik_plan.h), on the CPU.
+
+A small C++ program includes the plan header, makes forward and backward
+plans over a sweep of shapes and checks what the kernels rely on without
+checking it themselves:
+
+- all-pairs forward: units (document, chunk) dealt strided to workgroups
+  (unit k of group g is g + k * n_groups) cover every unit exactly once; no
+  workgroup holds more than 64 units (the wave-0 scan and the set-up loop) or
+  more schedule entries than the LDS schedule holds; chunks cover the
+  longest document; the grid covers every group and slot block;
+- pairs forward: chunks cover the document and the unit count matches;
+- workspace offsets are 256-byte aligned and inside the reported size;
+- fused grad_D: its LDS layout fits the size the plan reports and each
+  sorting wave ranks at most the hits it can hold.
+
+The numeric constants the kernels use (64 units, 32 entries per unit, 256
+threads, 8 sort-wave slots) are restated here as the kernels' own limits.
+"""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "maxsim_scoring_02_amd", "csrc")
+
+PROGRAM = r"""
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+#include "lik_plan.h"
+using namespace lik;
+
+static int fails = 0;
+#define CHECK(c, ...) do { if (!(c)) { if (fails < 20) { std::printf("FAIL %s: ", #c); \
+  std::printf(__VA_ARGS__); std::printf("\n"); } ++fails; } } while (0)
+
+static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, long dim, bool mask) {
+  FwdPlan p = make_fwd_plan(layout, elem, Nq, Lq, Nd, Ld, dim, mask, true);
+  if (p.Nq == 0 || p.n_docs == 0 || Lq == 0) return;
+  CHECK(p.SPW == 32 * p.NB, "SPW");
+  if (layout == kAllPairs) {
+    const long n_units = p.n_docs * p.nchunks;
+    CHECK(p.nchunks * p.tpc >= p.ntiles_max, "chunks %ld x %ld < tiles %ld", p.nchunks, p.tpc, p.ntiles_max);
+    CHECK(p.upw >= 1 && p.upw <= kApMaxDocs, "upw %ld", p.upw);
+    CHECK(p.n_groups * p.upw >= n_units, "groups x upw < units");
+    CHECK(p.n_groups <= n_units, "more groups than units");
+    CHECK(p.n_sb * 4 >= p.n_cg, "slot blocks");
+    CHECK(8 * p.gpx >= p.n_groups, "grid groups");
+    // strided assignment: every unit exactly once, capacities respected
+    std::vector<int> seen(n_units, 0);
+    for (long g = 0; g < p.n_groups; ++g) {
+      long n_my = (n_units - g + p.n_groups - 1) / p.n_groups;
+      if (n_my > p.upw) n_my = p.upw;
+      CHECK(n_my >= 1 && n_my <= kApMaxDocs, "n_my %ld", n_my);
+      long entries = 0;
+      for (long k = 0; k < n_my; ++k) {
+        const long u = g + k * p.n_groups;
+        CHECK(u < n_units, "unit %ld out of range", u);
+        if (u < n_units) seen[u]++;
+        const long c = u / p.n_docs;
+        const long t0 = c * p.tpc;
+        long t1 = t0 + p.tpc < p.ntiles_max ? t0 + p.tpc : p.ntiles_max;
+        if (t1 < t0) t1 = t0;
+        entries += t1 > t0 ? (t1 - t0 + 1) / 2 : 1;
+        CHECK((t1 - t0 + 1) / 2 <= 32, "entries per unit");
+      }
+      CHECK(entries <= kApMaxST, "entries %ld > %d", entries, kApMaxST);
+    }
+    for (long u = 0; u < n_units; ++u) CHECK(seen[u] == 1, "unit %ld seen %d times", u, seen[u]);
+    CHECK(p.n_docs <= kApMaxDocIndex || true, "docs");
+  } else {
+    CHECK(p.nchunks * p.tpc >= p.ntiles_max, "pairs chunks");
+    CHECK(p.n_units == p.n_docs * p.n_cg * p.nchunks, "pairs units");
+  }
+  const size_t offs[] = {p.off_bits, p.off_tiles, p.off_partM, p.off_partJ};
+  for (size_t o : offs) CHECK(o % 256 == 0 && o <= p.fwd_bytes, "fwd offset %zu / %zu", o, p.fwd_bytes);
+}
+
+static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, long dim) {
+  BwdPlan b = make_bwd_plan(layout, elem, Nq, Lq, Nd, Ld, dim, true, true);
+  if (b.fwd.Nq == 0 || b.fwd.n_docs == 0) return;
+  if (b.gd_mode == kGdFused) {
+    CHECK(b.fz_sw >= 1 && b.fz_sw <= kFzThreads / 64, "sort waves %d", b.fz_sw);
+    CHECK((b.H + b.fz_sw - 1) / b.fz_sw <= kFzMaxHitsPerWave, "hits per sort wave");
+    CHECK(b.fz_split >= 1 && b.fz_split <= 8, "split");
+    const size_t start = (size_t)(Ld + 1) * 4, sorted = (size_t)b.H * 4, gl = (size_t)Nq * 4;
+    CHECK(b.fz_off_cnt >= (int)start, "start area");
+    CHECK(b.fz_off_gl - b.fz_off_sorted >= (int)sorted, "sorted area");
+    CHECK(b.fz_off_union - b.fz_off_gl >= (int)gl, "gl area");
+    CHECK((size_t)b.fz_off_masks + (size_t)b.fz_sw * Ld * 8 <= b.fz_lds, "masks inside LDS");
+    CHECK(b.fz_lds <= 160 * 1024, "LDS %zu", b.fz_lds);
+  }
+  CHECK(b.total >= b.fwd.fwd_bytes || !b.recompute, "bwd total");
+}
+
+int main() {
+  const long dims[] = {64, 128, 256};
+  const long Lqs[] = {1, 7, 20, 32, 33, 64, 100};
+  const long Lds[] = {1, 31, 32, 33, 300, 1030, 2049, 2111, 8192, 32768};
+  const long Nqs[] = {1, 2, 16, 128, 256};
+  const long Nds[] = {1, 4, 75, 256, 1000};
+  for (int elem = 0; elem < 3; ++elem)
+    for (long dim : dims)
+      for (long Lq : Lqs)
+        for (long Ld : Lds)
+          for (long Nq : Nqs)
+            for (long Nd : Nds) {
+              fwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim, true);
+              fwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim, true);
+              fwd_case(kKd, elem, Nq, Lq, 16, Ld, dim, false);
+              if (Ld <= 16000) bwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim);
+            }
+  std::printf("fails %d\n", fails);
+  return fails ? 1 : 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs a host C++ compiler")
+def test_launch_plan_invariants(tmp_path):
+    src = tmp_path / "plan_check.cpp"
+    exe = tmp_path / "plan_check"
+    src.write_text(PROGRAM)
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-2000:]
+    assert "fails 0" in r.stdout
