@@ -137,8 +137,9 @@ class Op:
         else:
             self.dims = (w.Q.shape[0], Lq, w.D.shape[1], w.D.shape[2], dim)
             ops = (_lib.LIK_OP_KD_FWD, _lib.LIK_OP_KD_BWD)
-        flags_f = (1 if self.argmax is not None else 0) | (2 if self.dm is not None else 0)
-        flags_b = 1 | (2 if self.dm is not None else 0)
+        masks = (2 if self.dm is not None else 0) | (4 if self.qm is not None else 0)
+        flags_f = (1 if self.argmax is not None else 0) | masks
+        flags_b = 1 | masks
         self.wsf_n = self.L.lik_workspace_bytes(ops[0], *self.dims, self.dt, flags_f)
         self.wsb_n = self.L.lik_workspace_bytes(ops[1], *self.dims, self.dt, flags_b)
         mk = lambda n: torch.empty(max(n, 256), dtype=torch.uint8, device=dev)

@@ -120,6 +120,11 @@ lik_status lik_set_profile_events(void* start_event, void* stop_event);
  *              backward -- the caller passes the forward's argmax (if 0, the
  *              backward recomputes it into the workspace).
  * flags bit 1: a document mask will be passed.
+ * flags bit 2: a query mask will be passed (all-pairs: only valid query
+ *              tokens are scored, packed through a token list kept in the
+ *              workspace).
+ * A call whose masks or argmax differ from the flags the workspace was sized
+ * with may need more bytes; it then returns LIK_ERR_INVALID_ARG.
  * Returns 0 for zero-sized problems; never fails (returns SIZE_MAX for sizes
  * that overflow).
  */

@@ -112,6 +112,11 @@ def _embeddings(Q: torch.Tensor, D: torch.Tensor) -> int:
     return DTYPE_CODE[Q.dtype]
 
 
+def _flags(argmax_given: bool, dm, qm) -> int:
+    """lik_workspace_bytes flags: bit 0 argmax, bit 1 document mask, bit 2 query mask."""
+    return (1 if argmax_given else 0) | (2 if dm is not None else 0) | (4 if qm is not None else 0)
+
+
 def _mask(m: Optional[torch.Tensor], shape, device) -> Optional[torch.Tensor]:
     if m is None:
         return None
@@ -143,7 +148,7 @@ def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
     am = (torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=Q.device)
           if keep_argmax else None)
-    flags = (1 if keep_argmax else 0) | (2 if dm is not None else 0)
+    flags = _flags(keep_argmax, dm, qm)
     wsb = lib().lik_workspace_bytes(LIK_OP_FWD, Nq, Lq, Nd, Ld, dim, dt, flags)
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_fwd(_ptr(Q), _ptr(D), dt, Nq, Lq, Nd, Ld, dim, _ptr(qm), _ptr(dm),
@@ -162,7 +167,7 @@ def lik_maxsim_pairwise_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     dm = _mask(d_mask, (B, Ld), Q.device)
     scores = torch.empty((B,), dtype=torch.float32, device=Q.device)
     am = torch.empty((B, Lq), dtype=torch.int32, device=Q.device) if keep_argmax else None
-    flags = (1 if keep_argmax else 0) | (2 if dm is not None else 0)
+    flags = _flags(keep_argmax, dm, qm)
     wsb = lib().lik_workspace_bytes(LIK_OP_PAIRWISE_FWD, B, Lq, 1, Ld, dim, dt, flags)
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_pairwise_fwd(_ptr(Q), _ptr(D), dt, B, Lq, Ld, dim, _ptr(qm),
@@ -182,7 +187,7 @@ def lik_maxsim_kd_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     dm = _mask(d_mask, (B, N, Ld), Q.device)
     scores = torch.empty((B, N), dtype=torch.float32, device=Q.device)
     am = torch.empty((B, N, Lq), dtype=torch.int32, device=Q.device) if keep_argmax else None
-    flags = (1 if keep_argmax else 0) | (2 if dm is not None else 0)
+    flags = _flags(keep_argmax, dm, qm)
     wsb = lib().lik_workspace_bytes(LIK_OP_KD_FWD, B, Lq, N, Ld, dim, dt, flags)
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_kd_fwd(_ptr(Q), _ptr(D), dt, B, Lq, N, Ld, dim, _ptr(qm), _ptr(dm),
@@ -219,7 +224,7 @@ def lik_maxsim_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
     am = _argmax_in(argmax, (Nq, Nd, Lq), Q.device)
     gQ = torch.empty((Nq, Lq, dim), dtype=torch.float32, device=Q.device) if need_grad_q else None
     gD = torch.empty((Nd, Ld, dim), dtype=torch.float32, device=Q.device) if need_grad_d else None
-    flags = (1 if am is not None else 0) | (2 if dm is not None else 0)
+    flags = _flags(am is not None, dm, qm)
     wsb = lib().lik_workspace_bytes(LIK_OP_BWD, Nq, Lq, Nd, Ld, dim, dt, flags)
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_bwd(_ptr(Q), _ptr(D), dt, Nq, Lq, Nd, Ld, dim, _ptr(qm), _ptr(dm),
@@ -238,7 +243,7 @@ def lik_maxsim_pairwise_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=
     am = _argmax_in(argmax, (B, Lq), Q.device)
     gQ = torch.empty((B, Lq, dim), dtype=torch.float32, device=Q.device) if need_grad_q else None
     gD = torch.empty((B, Ld, dim), dtype=torch.float32, device=Q.device) if need_grad_d else None
-    flags = (1 if am is not None else 0) | (2 if dm is not None else 0)
+    flags = _flags(am is not None, dm, qm)
     wsb = lib().lik_workspace_bytes(LIK_OP_PAIRWISE_BWD, B, Lq, 1, Ld, dim, dt, flags)
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_pairwise_bwd(_ptr(Q), _ptr(D), dt, B, Lq, Ld, dim, _ptr(qm),
@@ -258,7 +263,7 @@ def lik_maxsim_kd_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
     am = _argmax_in(argmax, (B, N, Lq), Q.device)
     gQ = torch.empty((B, Lq, dim), dtype=torch.float32, device=Q.device) if need_grad_q else None
     gD = torch.empty((B, N, Ld, dim), dtype=torch.float32, device=Q.device) if need_grad_d else None
-    flags = (1 if am is not None else 0) | (2 if dm is not None else 0)
+    flags = _flags(am is not None, dm, qm)
     wsb = lib().lik_workspace_bytes(LIK_OP_KD_BWD, B, Lq, N, Ld, dim, dt, flags)
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_kd_bwd(_ptr(Q), _ptr(D), dt, B, Lq, N, Ld, dim, _ptr(qm), _ptr(dm),

@@ -136,7 +136,7 @@ lik_status forward_entry(int layout, const void* Q, const void* D, lik_dtype dty
   st = check_supported(dtype, s);
   if (st != LIK_OK) return st;
   lik::FwdPlan p = lik::make_fwd_plan(layout, (int)dtype, nq_or_b, Lq, nd_or_n, Ld, dim,
-                                      d_mask != nullptr, argmax != nullptr);
+                                      d_mask != nullptr, argmax != nullptr, q_mask != nullptr);
   if (ws_bytes < p.fwd_bytes)
     return fail(LIK_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                 p.fwd_bytes);
@@ -174,7 +174,7 @@ lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dt
     return fail(LIK_ERR_UNSUPPORTED, "backward supports Ld <= %lld (got %lld)",
                 (long long)kBwdMaxLd, (long long)Ld);
   lik::BwdPlan p = lik::make_bwd_plan(layout, (int)dtype, nq_or_b, Lq, nd_or_n, Ld, dim,
-                                      d_mask != nullptr, argmax != nullptr);
+                                      d_mask != nullptr, argmax != nullptr, q_mask != nullptr);
   if (ws_bytes < p.total)
     return fail(LIK_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                 p.total);
@@ -242,10 +242,13 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or
     return SIZE_MAX;
   const bool has_dmask = (flags & 2) != 0;
   const bool arg = (flags & 1) != 0;
+  const bool has_qmask = (flags & 4) != 0;
   if (!bwd)
-    return lik::make_fwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim, has_dmask, arg)
+    return lik::make_fwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim, has_dmask, arg,
+                              has_qmask)
         .fwd_bytes;
-  return lik::make_bwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim, has_dmask, arg)
+  return lik::make_bwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim, has_dmask, arg,
+                            has_qmask)
       .total;
 }
 

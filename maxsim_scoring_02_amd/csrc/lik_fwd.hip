@@ -71,6 +71,65 @@ __global__ void fill_scores_no_query_tokens_kernel(float* scores, int64_t n_out,
 }
 
 // ---------------------------------------------------------------------------
+// compacted query tokens: the valid (q, i) of the query mask in (q, i) order.
+// One workgroup walks the mask in blocks of 1024 x 16 tokens: a thread counts
+// its 16, a scan over the workgroup gives its first slot, and the running
+// total carries from block to block.  n <= 2^22.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void compact_prep_kernel(const uint8_t* __restrict__ q_mask,
+                                                            int64_t n, int32_t* __restrict__ tok,
+                                                            int32_t* __restrict__ inv,
+                                                            int32_t* __restrict__ cnt) {
+  constexpr int T = 1024, PER = 16, NWV = T / 64;
+  __shared__ int wsum[NWV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int64_t base = 0; base < n; base += (int64_t)T * PER) {
+    const int64_t t0 = base + (int64_t)tid * PER;
+    uint8_t m[PER];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int64_t j = t0 + k;
+      m[k] = j < n ? q_mask[j] : (uint8_t)0;
+      c += m[k] != 0;
+    }
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const int x = wsum[w];
+      if (w < wave) wbase += x;
+      total += x;
+    }
+    int slot = carry + wbase + incl - c;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int64_t j = t0 + k;
+      if (j < n) {
+        if (m[k]) {
+          tok[slot] = (int32_t)j;
+          inv[j] = slot;
+          ++slot;
+        } else {
+          inv[j] = -1;
+        }
+      }
+    }
+    carry += total;
+    __syncthreads();                       // wsum is rewritten by the next block
+  }
+  if (tid == 0) *cnt = carry;
+}
+
+// ---------------------------------------------------------------------------
 // slot mapping (all-pairs): wave gw, slot L -> (query q, token i)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool slot_qi(int64_t gw, int L, int SPW, int64_t qpw, int64_t Nq,
@@ -267,7 +326,26 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   const int sb = kx - (kx / n_sb) * n_sb;
   if (g >= a.n_groups || sb >= a.n_sb) return;
   const int gw = sb * kApNW + wave;
-  const bool active = gw < a.n_cg;
+  // compacted query tokens: slots past the last valid token hold nothing, and
+  // a workgroup with none of its slots below it leaves at once
+  const int64_t n_valid = a.compact ? (int64_t)*a.tok_cnt : 0;
+  if (a.compact && (int64_t)sb * kApNW * SPW >= n_valid) return;
+  const bool active = gw < a.n_cg && (!a.compact || (int64_t)gw * SPW < n_valid);
+  // slot L of this wave -> (query q, token i); false for an empty slot
+  auto slot_of = [&](int L, int64_t& q, int64_t& i) -> bool {
+    if (a.compact) {
+      const int64_t s2 = (int64_t)gw * SPW + L;
+      if (!active || s2 >= n_valid) {
+        q = i = 0;
+        return false;
+      }
+      const int64_t t = a.tok[s2];
+      q = t / a.Lq;
+      i = t - q * a.Lq;
+      return true;
+    }
+    return active && slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, q, i);
+  };
 
   // ---- the workgroup's units (document, chunk) and their super-tiles ----
   // A flat schedule in LDS: entry e = one super-tile (or one empty unit),
@@ -437,7 +515,7 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       int64_t q, i;
-      ok[b] = active && slot_qi(gw, b * 32 + r, SPW, a.qpw, a.Nq, a.Lq, q, i);
+      ok[b] = slot_of(b * 32 + r, q, i);
       rows[b] = ok[b] ? q * a.Lq + i : 0;
     }
     load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
@@ -446,7 +524,7 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   const int L = NB == 2 ? lane : (lane & 31);
   const bool writer = NB == 2 || lane < 32;
   int64_t slot_q = 0, slot_i = 0;
-  const bool slot_ok = active && slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, slot_q, slot_i);
+  const bool slot_ok = slot_of(L, slot_q, slot_i);
   const bool slot_tok = slot_ok && (!a.q_mask || a.q_mask[slot_q * a.Lq + slot_i]);
   const int seg_start = a.qpw > 0 ? (int)((L / a.Lq) * a.Lq) : 0;
   const bool seg_last = slot_ok && slot_i == a.Lq - 1;
@@ -735,7 +813,13 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
       const int64_t i = i0 + lane;
       const bool ok = i < a.Lq;
       int64_t cg, slot;
-      if (ap) {
+      bool have = ok;                        // this token has partials
+      if (ap && a.compact) {
+        const int32_t s2 = ok ? a.tok_inv[q * a.Lq + i] : -1;
+        have = s2 >= 0;
+        cg = have ? s2 / a.SPW : 0;
+        slot = have ? s2 - cg * a.SPW : 0;
+      } else if (ap) {
         if (a.qpw > 0) {
           cg = q / a.qpw;
           slot = (q - cg * a.qpw) * a.Lq + i;
@@ -750,7 +834,7 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
       }
       float M = -__builtin_inff();
       int J = -1;
-      if (ok) {
+      if (have) {
         const int64_t stride = a.n_docs * a.n_cg * a.SPW;      // between chunks
         const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
         constexpr int U = 4;
@@ -817,7 +901,13 @@ __global__ __launch_bounds__(256) void combine_fwd_wave_kernel(FwdArgs a) {
       const int64_t i = i0 + li;
       const bool ok = i < a.Lq;
       int64_t cg, slot;
-      if (ap) {
+      bool have = ok;                        // this token has partials
+      if (ap && a.compact) {
+        const int32_t s2 = ok ? a.tok_inv[q * a.Lq + i] : -1;
+        have = s2 >= 0;
+        cg = have ? s2 / a.SPW : 0;
+        slot = have ? s2 - cg * a.SPW : 0;
+      } else if (ap) {
         if (a.qpw > 0) {
           cg = q / a.qpw;
           slot = (q - cg * a.qpw) * a.Lq + i;
@@ -832,7 +922,7 @@ __global__ __launch_bounds__(256) void combine_fwd_wave_kernel(FwdArgs a) {
       }
       float M = -__builtin_inff();
       int J = -1;
-      if (ok) {
+      if (have) {
         const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
         constexpr int U = 4;
         for (int64_t c0 = 0; c0 < a.nchunks; c0 += U) {
@@ -971,6 +1061,16 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
   if (p.partial) {
     a.part_M = reinterpret_cast<float*>(ws + p.off_partM);
     a.part_J = reinterpret_cast<int32_t*>(ws + p.off_partJ);
+  }
+  if (p.compact) {
+    a.compact = 1;
+    a.tok = reinterpret_cast<int32_t*>(ws + p.off_tok);
+    a.tok_inv = reinterpret_cast<int32_t*>(ws + p.off_inv);
+    a.tok_cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+    hipLaunchKernelGGL(compact_prep_kernel, dim3(1), dim3(1024), 0, s, q_mask, p.Nq * p.Lq, a.tok,
+                       a.tok_inv, a.tok_cnt);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
   }
   hipError_t e;
   switch (p.elem) {

@@ -19,6 +19,12 @@ struct FwdArgs {
   int32_t* argmax;
   float* part_M;            // partial maxima  [nchunks][n_docs][n_cg][SPW]
   int32_t* part_J;          // partial argmaxes, same layout
+  // compacted query tokens (all-pairs with a query mask): slot s holds token
+  // tok[s] = q * Lq + i for s < *tok_cnt; tok_inv[q * Lq + i] is its slot or -1
+  int32_t* tok;
+  int32_t* tok_inv;
+  int32_t* tok_cnt;
+  int compact;
   int layout;
   int SPW;
   int partial;

@@ -25,6 +25,10 @@ struct FwdPlan {
   int64_t ntiles_max = 0;   // ceil(Ld / 32)
   bool has_dmask = false;
   bool partial = false;     // per-slot partials + combine kernel
+  // all-pairs with a query mask: only the valid query tokens get slots, packed
+  // in (query, token) order from a device-side list (n_cg is then an upper
+  // bound; workgroups past the last valid token leave at once)
+  bool compact = false;
   // slot mapping (all-pairs): qpw > 0 packs qpw whole queries per wave,
   // qpw == 0 flattens (q, i) so a query may span waves.
   int64_t qpw = 0;
@@ -36,7 +40,8 @@ struct FwdPlan {
   int64_t n_groups = 0, gpx = 0;
   int64_t n_units = 0;      // pairs: waves launched
   // workspace layout (bytes)
-  size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, fwd_bytes = 0;
+  size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, off_tok = 0, off_inv = 0,
+         off_cnt = 0, fwd_bytes = 0;
 };
 
 // grad_D strategies
@@ -87,9 +92,12 @@ inline int blocks_per_wave(int elem, int64_t dim) {
   return dim <= 128 ? 2 : 1;
 }
 
+// largest Nq * Lq whose valid tokens are compacted (one workgroup lists them)
+constexpr int64_t kCompactMaxTokens = int64_t(1) << 22;
+
 inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
                              int64_t nd_or_n, int64_t Ld, int64_t dim, bool has_dmask,
-                             bool keep_argmax) {
+                             bool keep_argmax, bool has_qmask = false) {
   (void)keep_argmax;
   FwdPlan p;
   p.layout = layout;
@@ -130,7 +138,11 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
   }
 
   if (layout == kAllPairs) {
-    if (Lq <= p.SPW) {
+    p.compact = has_qmask && Lq > 1 && p.Nq * Lq <= kCompactMaxTokens;
+    if (p.compact) {
+      p.qpw = 0;
+      p.n_cg = cdiv(p.Nq * Lq, p.SPW);
+    } else if (Lq <= p.SPW) {
       p.qpw = p.SPW / Lq;
       p.n_cg = cdiv(p.Nq, p.qpw);
     } else {
@@ -148,10 +160,12 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
       p.tpc = p.ntiles_max > 0 ? p.ntiles_max : 1;
       p.nchunks = 1;
     }
-    p.partial = (p.nchunks > 1) || (p.qpw == 0);
+    p.partial = (p.nchunks > 1) || (p.qpw == 0);   // compact has qpw == 0
     int64_t units = p.n_docs * p.nchunks;
     // About 1024 workgroups; each keeps its query fragments for upw units.
-    int64_t target = 1024;
+    // With compacted tokens the workgroups past the last valid token leave
+    // at once, so twice as many smaller ones keep the last round short.
+    int64_t target = p.compact ? 2048 : 1024;
     int64_t per_sb = cdiv(target, p.n_sb);
     p.upw = per_sb >= units ? 1 : cdiv(units, per_sb);
     if (p.upw < 1) p.upw = 1;
@@ -174,6 +188,15 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
     p.partial = (p.nchunks > 1) || (p.n_cg > 1);
     p.n_units = pairs * p.nchunks;
   }
+  if (p.compact) {
+    const size_t nt = (size_t)p.Nq * Lq;
+    p.off_tok = off;
+    off = align256(off + nt * 4);
+    p.off_inv = off;
+    off = align256(off + nt * 4);
+    p.off_cnt = off;
+    off = align256(off + 4);
+  }
   if (p.partial) {
     size_t n = (size_t)p.nchunks * p.n_docs * p.n_cg * p.SPW;
     p.off_partM = off;
@@ -186,9 +209,10 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
 }
 
 inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, int64_t nd_or_n,
-                             int64_t Ld, int64_t dim, bool has_dmask, bool have_argmax) {
+                             int64_t Ld, int64_t dim, bool has_dmask, bool have_argmax,
+                             bool has_qmask = false) {
   BwdPlan b;
-  b.fwd = make_fwd_plan(layout, elem, nq_or_b, Lq, nd_or_n, Ld, dim, has_dmask, true);
+  b.fwd = make_fwd_plan(layout, elem, nq_or_b, Lq, nd_or_n, Ld, dim, has_dmask, true, has_qmask);
   const FwdPlan& f = b.fwd;
   if (f.Nq == 0 || f.n_docs == 0) return b;
   b.recompute = !have_argmax;

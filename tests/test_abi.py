@@ -89,6 +89,20 @@ def test_forward_rejects_small_workspace(L):
     assert fwd(L, dm=FAKE, ws=None, wsb=need) == LIK_ERR_INVALID_ARG
 
 
+def test_query_mask_needs_its_token_tables(L):
+    # all-pairs with a query mask lists the valid tokens in the workspace, so
+    # a workspace sized without flag bit 2 is too small for such a call
+    plain = L.lik_workspace_bytes(LIK_OP_FWD, 2, 32, 3, 40, 128, LIK_BF16, 1)
+    masked = L.lik_workspace_bytes(LIK_OP_FWD, 2, 32, 3, 40, 128, LIK_BF16, 1 | 4)
+    assert masked >= plain + 2 * 2 * 32 * 4
+    assert fwd(L, qm=FAKE, argmax=FAKE, wsb=plain) == LIK_ERR_INVALID_ARG
+    assert "workspace too small" in L.lik_last_error().decode()
+    # pairwise and kd score every query token in place: no tables
+    for op in (LIK_OP_PAIRWISE_FWD, LIK_OP_KD_FWD):
+        assert (L.lik_workspace_bytes(op, 8, 32, 4, 1030, 128, LIK_BF16, 1 | 4) ==
+                L.lik_workspace_bytes(op, 8, 32, 4, 1030, 128, LIK_BF16, 1))
+
+
 def test_unsupported_dim_is_reported_before_device_work(L):
     assert fwd(L, dim=100) == LIK_ERR_UNSUPPORTED
     assert "dim" in L.lik_last_error().decode()

@@ -11,6 +11,8 @@ checking it themselves:
   longest document; the grid covers every group and slot block;
 - pairs forward: chunks cover the document and the unit count matches;
 - workspace offsets are 256-byte aligned and inside the reported size;
+- a query mask switches all-pairs to compacted token slots: split path,
+  slots for every token, token tables inside the workspace;
 - fused grad_D: its LDS layout fits the size the plan reports and each
   sorting wave ranks at most the hits it can hold.
 
@@ -38,10 +40,21 @@ static int fails = 0;
 #define CHECK(c, ...) do { if (!(c)) { if (fails < 20) { std::printf("FAIL %s: ", #c); \
   std::printf(__VA_ARGS__); std::printf("\n"); } ++fails; } } while (0)
 
-static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, long dim, bool mask) {
-  FwdPlan p = make_fwd_plan(layout, elem, Nq, Lq, Nd, Ld, dim, mask, true);
+static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, long dim, bool mask,
+                     bool qmask = false) {
+  FwdPlan p = make_fwd_plan(layout, elem, Nq, Lq, Nd, Ld, dim, mask, true, qmask);
   if (p.Nq == 0 || p.n_docs == 0 || Lq == 0) return;
   CHECK(p.SPW == 32 * p.NB, "SPW");
+  if (p.compact) {
+    CHECK(layout == kAllPairs && qmask, "compact only for all-pairs with a query mask");
+    CHECK(p.partial && p.qpw == 0, "compact uses the split path");
+    CHECK(p.n_cg * p.SPW >= p.Nq * Lq, "compact slots cover every token");
+    CHECK(p.off_tok % 256 == 0 && p.off_inv >= p.off_tok + (size_t)p.Nq * Lq * 4 &&
+              p.off_cnt >= p.off_inv + (size_t)p.Nq * Lq * 4 && p.off_cnt + 4 <= p.fwd_bytes,
+          "compact tables");
+  } else if (layout == kAllPairs && qmask && Lq > 1) {
+    CHECK(p.Nq * Lq > kCompactMaxTokens, "a query mask compacts unless the token list is too long");
+  }
   if (layout == kAllPairs) {
     const long n_units = p.n_docs * p.nchunks;
     CHECK(p.nchunks * p.tpc >= p.ntiles_max, "chunks %ld x %ld < tiles %ld", p.nchunks, p.tpc, p.ntiles_max);
@@ -76,7 +89,8 @@ static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     CHECK(p.nchunks * p.tpc >= p.ntiles_max, "pairs chunks");
     CHECK(p.n_units == p.n_docs * p.n_cg * p.nchunks, "pairs units");
   }
-  const size_t offs[] = {p.off_bits, p.off_tiles, p.off_partM, p.off_partJ};
+  const size_t offs[] = {p.off_bits, p.off_tiles, p.off_partM, p.off_partJ, p.off_tok, p.off_inv,
+                         p.off_cnt};
   for (size_t o : offs) CHECK(o % 256 == 0 && o <= p.fwd_bytes, "fwd offset %zu / %zu", o, p.fwd_bytes);
 }
 
@@ -110,6 +124,7 @@ int main() {
           for (long Nq : Nqs)
             for (long Nd : Nds) {
               fwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim, true);
+              fwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim, Nd % 2 == 0, true);
               fwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim, true);
               fwd_case(kKd, elem, Nq, Lq, 16, Ld, dim, false);
               if (Ld <= 16000) bwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim);
