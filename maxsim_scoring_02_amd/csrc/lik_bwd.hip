@@ -20,8 +20,8 @@
 //                          its hits by row in LDS, then lane groups sum equal
 //                          shares of the sorted hits; rows cut by a share
 //                          boundary are finished by the group where they start
-//     gradd_pairs_kernel   pairwise / kd: a wave per document streams the
-//                          (mostly zero) rows and sums the few hit rows inline
+//     gradd_pairs_kernel   pairwise / kd: four waves per document stream its
+//                          (mostly zero) rows and sum the few hit rows inline
 //     gradd_sort_*_kernel + gradd_rows_group_kernel
 //                          general fallback through the workspace
 #include <hip/hip_runtime.h>
@@ -808,11 +808,12 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ---------------------------------------------------------------------------
-// grad_D, pairwise / kd: one wave per document.  A document has only Lq hits
-// (one per query token), so its gradient is Ld rows of which at most Lq are
-// non-zero: the wave streams the rows in order with non-temporal stores and,
-// for a row some hit points at, adds g * Q[h] over those hits in increasing
-// h (their lanes, found by ballot) before storing it.
+// grad_D, pairwise / kd: four waves per document, each over a contiguous
+// quarter of its rows.  A document has only Lq hits (one per query token), so
+// its gradient is Ld rows of which at most Lq are non-zero: a wave streams its
+// rows in order with non-temporal stores and, for a row some hit points at,
+// adds g * Q[h] over those hits in increasing h (their lanes, found by
+// ballot) before storing it.
 // ---------------------------------------------------------------------------
 
 template <Elem E>
@@ -839,6 +840,8 @@ template <> __device__ __forceinline__ void load4_as_float<Elem::F32>(const char
   f[3] = w.w;
 }
 
+constexpr int kGdPairsParts = 4;
+
 template <Elem E, int DIM>
 __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
   constexpr int F4 = DIM / 4;                 // float4 per gradient row
@@ -847,9 +850,16 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
   constexpr int ES = ElemInfo<E>::kBytes;
   static_assert(F4 <= 64, "one gradient row per wave store at most");
   const int lane = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // kGdPairsParts waves per document, each streaming a contiguous share of its
+  // rows (whole stores of RPI rows), so enough stores are in flight
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t e = wv / kGdPairsParts;
+  const int part = (int)(wv - e * kGdPairsParts);
   if (e >= a.n_docs) return;
   const int Lq = (int)a.Lq, Ld = (int)a.Ld;
+  const int n_st = (Ld + RPI - 1) / RPI;                  // stores per document
+  const int r_begin = (int)((int64_t)n_st * part / kGdPairsParts) * RPI;
+  const int r_end = min((int)((int64_t)n_st * (part + 1) / kGdPairsParts) * RPI, Ld);
   const int nh = (Lq + 63) / 64;
   const float g = a.g[e];
   const int64_t qbase = (e / a.K) * a.Lq;     // first Q row of this document's query
@@ -864,7 +874,7 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
   const int sub = lane / F4, f = lane - (lane / F4) * F4;
   float* out = a.gD + e * (int64_t)Ld * DIM;
   const char* Qb = (const char*)a.Q;
-  for (int r0 = 0; r0 < Ld; r0 += RPI) {
+  for (int r0 = r_begin; r0 < r_end; r0 += RPI) {
     bool any = false;
 #pragma unroll
     for (int k = 0; k < NH; ++k) any |= (k < nh) && key[k] >= r0 && key[k] < r0 + RPI;
@@ -889,7 +899,7 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
       }
     }
     const int row = r0 + sub;
-    if (sub < RPI && row < Ld) {
+    if (sub < RPI && row < r_end) {
       const f32x4 w = {v[0], v[1], v[2], v[3]};
       __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f));
     }
@@ -948,8 +958,8 @@ static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t fz_lds, hipStr
     return hipGetLastError();
   }
   if (mode == kGdPairs) {
-    hipLaunchKernelGGL((gradd_pairs_kernel<E, DIM>), dim3((unsigned)cdiv(a.n_docs, 4)), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL((gradd_pairs_kernel<E, DIM>),
+                       dim3((unsigned)cdiv(a.n_docs * kGdPairsParts, 4)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   if (a.Ld <= kSortWavesMaxLd) {
