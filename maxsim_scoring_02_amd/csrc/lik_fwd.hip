@@ -24,39 +24,76 @@ namespace lik {
 constexpr float kEmptyDocScore = -1e9f;
 
 // ---------------------------------------------------------------------------
-// mask prep: one wave per document.  A wave reads 64 consecutive mask bytes
-// (one per lane, coalesced) and a ballot of "byte != 0" is directly two tile
-// words; U blocks are read before any is used.
+// mask prep: one workgroup of 4 waves per document; every load is issued
+// before any is used, and the last valid word is the maximum over the waves.
+// - byte path: a wave reads 64 consecutive mask bytes (one per lane) and a
+//   ballot of "byte != 0" is directly two tile words;
+// - dword path (mask rows 4-byte aligned): a lane reads 4 bytes, forms their
+//   4 validity bits, and the 8 lanes of a 32-byte word OR their nibbles
+//   together by three lane exchanges, so a wave load covers 8 words.
 // ---------------------------------------------------------------------------
+template <bool DW>
 __global__ __launch_bounds__(256) void mask_prep_kernel(const uint8_t* __restrict__ d_mask,
                                                         int64_t n_docs, int64_t Ld, int64_t nwords,
                                                         uint32_t* __restrict__ bits,
                                                         int32_t* __restrict__ ntiles) {
-  constexpr int U = 8;
-  const int lane = threadIdx.x & 63;
-  const int64_t d = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (d >= n_docs) return;                        // whole wave
+  constexpr int U = 16, NWV = 4;
+  constexpr int kBlk = DW ? 256 : 64;             // bytes per wave load
+  __shared__ int s_last[NWV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t d = blockIdx.x;
+  if (d >= n_docs) return;                        // whole workgroup
   const uint8_t* m = d_mask + d * Ld;
   uint32_t* out = bits + d * nwords;
-  const int64_t nblk = (Ld + 63) / 64;
-  int last = -1;                                  // last word with a valid row (wave-uniform)
-  for (int64_t b0 = 0; b0 < nblk; b0 += U) {
-    uint8_t v[U];
+  const int64_t nblk = (Ld + kBlk - 1) / kBlk;
+  int last = -1;                                  // last word with a valid row
+  for (int64_t b0 = wave; b0 < nblk; b0 += (int64_t)NWV * U) {
+    if constexpr (DW) {
+      uint32_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = (b0 + u) * 64 + lane;
-      v[u] = j < Ld ? m[j] : (uint8_t)0;
-    }
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = (b0 + (int64_t)u * NWV) * kBlk + 4 * lane;   // Ld % 4 == 0: j + 3 < Ld or j >= Ld
+        v[u] = j < Ld ? *reinterpret_cast<const uint32_t*>(m + j) : 0u;
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t bal = __ballot(v[u] != 0);
-      const int64_t w = 2 * (b0 + u);
-      if (lane < 2 && w + lane < nwords) out[w + lane] = (uint32_t)(bal >> (32 * lane));
-      if (bal >> 32) last = (int)w + 1;
-      else if (bal) last = (int)w;
+      for (int u = 0; u < U; ++u) {
+        uint32_t nib = ((v[u] & 0xffu) != 0) | (((v[u] >> 8) & 0xffu) != 0) << 1 |
+                       (((v[u] >> 16) & 0xffu) != 0) << 2 | ((v[u] >> 24) != 0) << 3;
+        uint32_t word = nib << (4 * (lane & 7));
+        word |= __shfl_xor(word, 1);
+        word |= __shfl_xor(word, 2);
+        word |= __shfl_xor(word, 4);
+        const int64_t w = (b0 + (int64_t)u * NWV) * 8 + (lane >> 3);
+        if ((lane & 7) == 0 && w < nwords) out[w] = word;
+        if (word != 0u && w < nwords) last = max(last, (int)w);
+      }
+    } else {
+      uint8_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = (b0 + (int64_t)u * NWV) * kBlk + lane;
+        v[u] = j < Ld ? m[j] : (uint8_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t bal = __ballot(v[u] != 0);
+        const int64_t w = 2 * (b0 + (int64_t)u * NWV);
+        if (lane < 2 && w + lane < nwords) out[w + lane] = (uint32_t)(bal >> (32 * lane));
+        if (bal >> 32) last = max(last, (int)w + 1);
+        else if (bal) last = max(last, (int)w);
+      }
     }
   }
-  if (lane == 0) ntiles[d] = last + 1;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) last = max(last, __shfl_xor(last, k));
+  if (lane == 0) s_last[wave] = last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int l = s_last[0];
+#pragma unroll
+    for (int k = 1; k < NWV; ++k) l = max(l, s_last[k]);
+    ntiles[d] = l + 1;
+  }
 }
 
 // scores when no query has tokens (Lq == 0): 0, or -1e9 for empty documents
@@ -1040,14 +1077,14 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
   if (p.has_dmask && p.n_docs > 0) {
     a.bits = reinterpret_cast<uint32_t*>(ws + p.off_bits);
     a.ntiles = reinterpret_cast<int32_t*>(ws + p.off_tiles);
-    if (p.nwords > 0) {
-      hipLaunchKernelGGL(mask_prep_kernel, dim3((unsigned)cdiv(p.n_docs, 4)), dim3(256), 0, s,
+    // (with Ld == 0 it only records that every document is empty)
+    const bool dw = p.Ld % 4 == 0 && (reinterpret_cast<uintptr_t>(d_mask) & 3u) == 0;
+    if (dw)
+      hipLaunchKernelGGL(mask_prep_kernel<true>, dim3((unsigned)p.n_docs), dim3(256), 0, s, d_mask,
+                         p.n_docs, p.Ld, p.nwords, a.bits, a.ntiles);
+    else
+      hipLaunchKernelGGL(mask_prep_kernel<false>, dim3((unsigned)p.n_docs), dim3(256), 0, s,
                          d_mask, p.n_docs, p.Ld, p.nwords, a.bits, a.ntiles);
-    } else {
-      // Ld == 0: every document is empty
-      hipLaunchKernelGGL(mask_prep_kernel, dim3((unsigned)cdiv(p.n_docs, 4)), dim3(256), 0, s,
-                         d_mask, p.n_docs, p.Ld, p.nwords, a.bits, a.ntiles);
-    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
