@@ -1,6 +1,7 @@
 // Forward kernels of the gfx950 MaxSim scorer.
 //
 //   mask_prep       bool document mask -> 32-bit tile words + tile count
+//   compact_prep    bool query mask -> list of the valid query tokens (all-pairs)
 //   allpairs_fwd    MFMA S^T tiles for every (query, doc), doc tiles shared
 //                   through LDS by the workgroup's waves (compute-bound shapes)
 //   pairs_fwd       pairwise / kd: one wave streams its own document
@@ -208,11 +209,12 @@ constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4
 //
 // A workgroup of 4 waves holds 4 x SPW query-token slots in registers (the
 // MFMA B operand) and streams document super-tiles of 2 x 32 rows through a
-// double-buffered LDS ring (padded rows), one barrier per super-tile.  Tiles
-// arrive by buffer loads whose descriptor covers only the unit's remaining
-// rows, so rows past the end read as zeros (and are masked) with no per-lane
-// bounds arithmetic.  Two workgroups fit on a CU, so the waves sharing a SIMD
-// run in independent phases and one's MFMAs overlap the other's VALU work.
+// three-stage LDS ring (padded rows), one barrier per super-tile.  Tiles are
+// copied global -> LDS by buffer loads whose descriptor covers only the
+// unit's remaining rows, so rows past the end read as zeros (and are masked)
+// with no per-lane bounds arithmetic.  Two workgroups fit on a CU, so the
+// waves sharing a SIMD run in independent phases and one's MFMAs overlap the
+// other's VALU work.
 // ---------------------------------------------------------------------------
 constexpr int kApNW = 4;                       // waves per workgroup
 constexpr int kApThreads = kApNW * kWave;

@@ -48,7 +48,7 @@ struct FwdPlan {
 enum GdMode : int {
   kGdSort = 0,    // sort kernel + row kernel through the workspace (any shape)
   kGdFused = 1,   // all-pairs: one fused kernel per document, sort in LDS
-  kGdPairs = 2    // pairwise / kd: one wave per document streams its rows
+  kGdPairs = 2    // pairwise / kd: four waves per document stream its rows
 };
 constexpr int kFzThreads = 512;        // threads of the fused grad_D workgroup
 constexpr int kFzMaxHitsPerWave = 2048; // hits one sorting wave of it ranks
