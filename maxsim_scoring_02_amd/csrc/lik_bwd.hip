@@ -147,35 +147,38 @@ __global__ __launch_bounds__(256) void gradq_xcd_kernel(BwdArgs a) {
   float acc[EPC];
 #pragma unroll
   for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-  // round r: lane c of a token loads the index and weight of document
-  // k0 + c; every lane of the token then takes all U of them by lane swaps
-  auto fetch_idx = [&](int64_t k0, int& j, float& w) {
+  // round r: lane c of a token loads the index and weight of document k0 + c
+  // and turns them into a row of the slice (row 0 and weight 0 when the
+  // document has no valid row for this token); every lane of the token then
+  // takes all U of them by lane swaps and gathers with no further checks
+  const char* Ds = Db + d0 * a.Ld * (int64_t)G::kRowBytes;
+  auto fetch_idx = [&](int64_t k0, int& row, float& w) {
     const int64_t d = k0 + c;
-    j = -1;
+    row = 0;
     w = 0.0f;
     if (c < U && d < d1) {
       const int64_t p = q * Nd + d;
-      j = a.argmax[p * a.Lq + i];
-      w = a.g[p];
+      const int j = a.argmax[p * a.Lq + i];
+      if (j >= 0 && j < a.Ld) {
+        row = (int)((d - d0) * a.Ld + j);
+        w = a.g[p];
+      }
     }
   };
-  int jn;
+  int rn;
   float wn;
-  fetch_idx(d0, jn, wn);
+  fetch_idx(d0, rn, wn);
   for (int64_t k0 = d0; k0 < d1; k0 += U) {
-    const int jc = jn;
+    const int rc = rn;
     const float wc = wn;
-    fetch_idx(k0 + U, jn, wn);             // next round's indices in flight
+    fetch_idx(k0 + U, rn, wn);             // next round's indices in flight
     u32x4 ch[U];
     float gg[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = __shfl(jc, base_lane + u);
-      const float w = __shfl(wc, base_lane + u);
-      const bool ok = j >= 0 && j < a.Ld;
-      const int64_t d = ok ? k0 + u : 0;
-      ch[u] = ld_global_16(Db + (d * a.Ld + (ok ? j : 0)) * (int64_t)G::kRowBytes + c * 16);
-      gg[u] = ok ? w : 0.0f;
+      const int row = __shfl(rc, base_lane + u);
+      gg[u] = __shfl(wc, base_lane + u);
+      ch[u] = ld_global_16(Ds + (int64_t)row * G::kRowBytes + c * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -262,7 +262,10 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
   } else if (layout != kAllPairs && Lq > 0 && Lq <= kPairsMaxLq && Ld > 0) {
     b.gd_mode = kGdPairs;
   }
-  if (layout == kAllPairs && f.n_docs >= kGqSliceMinDocs && Lq > 0 && Ld > 0) b.gq_slices = 8;
+  // (rows of one slice are indexed with 32 bits)
+  if (layout == kAllPairs && f.n_docs >= kGqSliceMinDocs && Lq > 0 && Ld > 0 &&
+      cdiv(f.n_docs, 8) * Ld < (int64_t(1) << 31))
+    b.gq_slices = 8;
 
   size_t off = 0;
   if (b.recompute && Lq > 0) {
