@@ -114,6 +114,9 @@ lik_status check_supported(lik_dtype dtype, const Shapes& s) {
     return fail(LIK_ERR_UNSUPPORTED, "all-pairs supports Nd <= %lld and Ld <= %lld (got %lld, %lld)",
                 (long long)lik::kApMaxDocIndex, (long long)lik::kApMaxLd, (long long)s.nd_or_n,
                 (long long)s.Ld);
+  if (s.layout == lik::kAllPairs && s.Lq > 0 && s.nq_or_b > lik::kApMaxTokens / s.Lq)
+    return fail(LIK_ERR_UNSUPPORTED, "all-pairs supports Nq * Lq <= %lld (got %lld x %lld)",
+                (long long)lik::kApMaxTokens, (long long)s.nq_or_b, (long long)s.Lq);
   return LIK_OK;
 }
 

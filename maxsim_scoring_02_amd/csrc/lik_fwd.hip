@@ -170,17 +170,18 @@ __global__ __launch_bounds__(1024) void compact_prep_kernel(const uint8_t* __res
 // ---------------------------------------------------------------------------
 // slot mapping (all-pairs): wave gw, slot L -> (query q, token i)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool slot_qi(int64_t gw, int L, int SPW, int64_t qpw, int64_t Nq,
-                                        int64_t Lq, int64_t& q, int64_t& i) {
+__device__ __forceinline__ bool slot_qi(int gw, int L, int SPW, int qpw, int Nq, int Lq, int& q,
+                                        int& i) {
+  // 32-bit throughout: the plan keeps Nq * Lq below 2^31
   if (qpw > 0) {
-    int64_t k = L / Lq;
+    const int k = (int)((uint32_t)L / (uint32_t)Lq);
     i = L - k * Lq;
     q = gw * qpw + k;
     return k < qpw && q < Nq;
   }
-  int64_t s = gw * SPW + L;
-  q = s / Lq;
-  i = s - q * Lq;
+  const uint32_t s = (uint32_t)gw * (uint32_t)SPW + (uint32_t)L;
+  q = (int)(s / (uint32_t)Lq);
+  i = (int)(s - (uint32_t)q * (uint32_t)Lq);
   return q < Nq;
 }
 
@@ -371,6 +372,7 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   if (a.compact && (int64_t)sb * kApNW * SPW >= n_valid) return;
   const bool active = gw < a.n_cg && (!a.compact || (int64_t)gw * SPW < n_valid);
   // slot L of this wave -> (query q, token i); false for an empty slot
+  const int Lq32 = (int)a.Lq;
   auto slot_of = [&](int L, int64_t& q, int64_t& i) -> bool {
     if (a.compact) {
       const int64_t s2 = (int64_t)gw * SPW + L;
@@ -378,12 +380,17 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
         q = i = 0;
         return false;
       }
-      const int64_t t = a.tok[s2];
-      q = t / a.Lq;
-      i = t - q * a.Lq;
+      const uint32_t t = (uint32_t)a.tok[s2];
+      const uint32_t q32 = t / (uint32_t)Lq32;
+      q = q32;
+      i = t - q32 * (uint32_t)Lq32;
       return true;
     }
-    return active && slot_qi(gw, L, SPW, a.qpw, a.Nq, a.Lq, q, i);
+    int q32 = 0, i32 = 0;
+    const bool ok = active && slot_qi(gw, L, SPW, (int)a.qpw, (int)a.Nq, Lq32, q32, i32);
+    q = q32;
+    i = i32;
+    return ok;
   };
 
   // ---- the workgroup's units (document, chunk) and their super-tiles ----
@@ -396,12 +403,20 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   // out strided (unit k of this workgroup is g + k * n_groups), so every
   // workgroup gets about as many units of each chunk index: a mix of long,
   // partial and empty chunks.
-  const int64_t n_grp = a.n_groups;
-  const int n_my = (int)min((int64_t)a.upw, (n_units - g + n_grp - 1) / n_grp);
+  // unit numbers stay below 2^31 (documents < 2^23, chunks < 256): 32-bit
+  // arithmetic, and no division at all when documents are not split
+  const uint32_t n_grp = (uint32_t)a.n_groups, n_docs32 = (uint32_t)a.n_docs;
+  const int n_my = (int)min((uint32_t)a.upw, ((uint32_t)n_units - g + n_grp - 1) / n_grp);
   auto unit_dc = [&](int k, int& d, int& c) {
-    const int64_t u = g + (int64_t)k * n_grp;
-    c = (int)(u / a.n_docs);
-    d = (int)(u - (int64_t)c * a.n_docs);
+    const uint32_t u = (uint32_t)g + (uint32_t)k * n_grp;
+    if (nchunks == 1) {
+      c = 0;
+      d = (int)u;
+    } else {
+      const uint32_t cu = u / n_docs32;
+      c = (int)cu;
+      d = (int)(u - cu * n_docs32);
+    }
   };
   const int Ld = (int)a.Ld;
   __shared__ int s_meta[kApMaxST];     // t | two << 24 | start << 25 | end << 26 | has << 27
@@ -565,7 +580,7 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   int64_t slot_q = 0, slot_i = 0;
   const bool slot_ok = slot_of(L, slot_q, slot_i);
   const bool slot_tok = slot_ok && (!a.q_mask || a.q_mask[slot_q * a.Lq + slot_i]);
-  const int seg_start = a.qpw > 0 ? (int)((L / a.Lq) * a.Lq) : 0;
+  const int seg_start = a.qpw > 0 ? (int)(((uint32_t)L / (uint32_t)Lq32) * (uint32_t)Lq32) : 0;
   const bool seg_last = slot_ok && slot_i == a.Lq - 1;
   // queries of 32 tokens two to a wave: their sums are lane-aligned halves
   const bool fast_sum = a.qpw > 0 && a.Lq == 32;

@@ -81,6 +81,8 @@ constexpr int kApMaxWords = 1024;
 // 2^23, chunks of 1024 rows below 256
 constexpr int64_t kApMaxDocIndex = (int64_t(1) << 23) - 1;
 constexpr int64_t kApMaxLd = 255 * 1024;
+// all-pairs query-token slots are numbered in 32-bit arithmetic
+constexpr int64_t kApMaxTokens = int64_t(1) << 30;
 // schedule entries: a super-tile (2 tiles) each, or one per empty unit
 constexpr int kApMaxST = kApMaxWords / 2 + 2 * kApMaxDocs;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
