@@ -220,6 +220,117 @@ __device__ __forceinline__ void state_fold_sparse(BlockState& s, const f32x16& a
   }
 }
 
+// ---------------------------------------------------------------------------
+// Lean fold for the all-pairs hot loop.  VALU time there adds to MFMA time
+// almost one for one, so the fold is written to issue as few VALU
+// instructions as possible:
+// - a 3-input max tree written directly (the generic fmax path re-quiets
+//   NaNs of unknown operands first; inputs are finite or -inf here);
+// - the copy of the improving tile runs under an exec mask of the improving
+//   lanes inside one asm statement whose operands are tied to the state's
+//   registers, so the state is updated in place (a divergent branch around
+//   the copy makes the compiler move all 16 values on every fold);
+// - a unit starts by resetting only the running max and tile.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max16_lean(const f32x16& x) {
+  const float m1 = vmax3(x[0], x[1], x[2]), m2 = vmax3(x[3], x[4], x[5]);
+  const float m3 = vmax3(x[6], x[7], x[8]), m4 = vmax3(x[9], x[10], x[11]);
+  const float m5 = vmax3(x[12], x[13], x[14]);
+  return vmax2(vmax3(m1, m2, m3), vmax3(m4, m5, x[15]));
+}
+
+// dst[O..O+7] = (useb ? b : a)[O..O+7] in the lanes of `lanes` (a subset of
+// the active lanes, from a ballot); other lanes keep dst.  exec is narrowed
+// and restored inside the statement, with no SCC write.
+template <int O>
+__device__ __forceinline__ void sel_copy8(float (&dst)[16], const f32x16& a, const f32x16& b,
+                                          uint64_t lanes, uint64_t useb) {
+  uint64_t sv;
+  asm("s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b64 exec, %[ln]\n\t"
+      "v_cndmask_b32_e64 %[d0], %[a0], %[b0], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d1], %[a1], %[b1], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d2], %[a2], %[b2], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d3], %[a3], %[b3], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d4], %[a4], %[b4], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d5], %[a5], %[b5], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d6], %[a6], %[b6], %[ub]\n\t"
+      "v_cndmask_b32_e64 %[d7], %[a7], %[b7], %[ub]\n\t"
+      "s_mov_b64 exec, %[sv]"
+      : [sv] "=&s"(sv), [d0] "+v"(dst[O + 0]), [d1] "+v"(dst[O + 1]), [d2] "+v"(dst[O + 2]),
+        [d3] "+v"(dst[O + 3]), [d4] "+v"(dst[O + 4]), [d5] "+v"(dst[O + 5]),
+        [d6] "+v"(dst[O + 6]), [d7] "+v"(dst[O + 7])
+      : [ln] "s"(lanes), [ub] "s"(useb), [a0] "v"(a[O + 0]), [b0] "v"(b[O + 0]),
+        [a1] "v"(a[O + 1]), [b1] "v"(b[O + 1]), [a2] "v"(a[O + 2]), [b2] "v"(b[O + 2]),
+        [a3] "v"(a[O + 3]), [b3] "v"(b[O + 3]), [a4] "v"(a[O + 4]), [b4] "v"(b[O + 4]),
+        [a5] "v"(a[O + 5]), [b5] "v"(b[O + 5]), [a6] "v"(a[O + 6]), [b6] "v"(b[O + 6]),
+        [a7] "v"(a[O + 7]), [b7] "v"(b[O + 7]));
+}
+
+// Start of a unit: only the running max and the tile are reset.  The 16
+// values are written by the first fold that improves on -inf; a lane that
+// never improves (no valid row of its half in the unit) keeps run_max = -inf,
+// and its resolved row is then never used (a valid row of the other half,
+// or the empty-document rule, decides).
+__device__ __forceinline__ void state_begin(BlockState& s, int t0) {
+  s.run_max = -__builtin_inff();
+  s.best_tile = t0;
+}
+
+// Fold tiles t and t+1 (strict '>' keeps the earlier tile, and within the
+// pair the earlier tile wins ties).
+__device__ __forceinline__ void state_fold_pair_lean(BlockState& s, const f32x16& xa,
+                                                     const f32x16& xb, int t) {
+  const float ta = max16_lean(xa), tb = max16_lean(xb);
+  const float tm = vmax2(ta, tb);
+  const bool better = tm > s.run_max;
+  const bool useb = tb > ta;
+  const uint64_t lanes = __builtin_amdgcn_ballot_w64(better);
+  const uint64_t ub = __builtin_amdgcn_ballot_w64(useb);
+  s.run_max = better ? tm : s.run_max;
+  s.best_tile = better ? t + (int)useb : s.best_tile;
+  sel_copy8<0>(s.best_val, xa, xb, lanes, ub);
+  sel_copy8<8>(s.best_val, xa, xb, lanes, ub);
+}
+
+// Fold one tile t.
+__device__ __forceinline__ void state_fold_one_lean(BlockState& s, const f32x16& x, int t) {
+  const float tm = max16_lean(x);
+  const bool better = tm > s.run_max;
+  const uint64_t lanes = __builtin_amdgcn_ballot_w64(better);
+  s.run_max = better ? tm : s.run_max;
+  s.best_tile = better ? t : s.best_tile;
+  sel_copy8<0>(s.best_val, x, x, lanes, 0);
+  sel_copy8<8>(s.best_val, x, x, lanes, 0);
+}
+
+// Fold one step of the hot loop: tiles t and t+1 when `two`, else tile t
+// alone (xb ignored); nothing when `step` is false.
+__device__ __forceinline__ void state_fold_step(BlockState& s, const f32x16& xa,
+                                                const f32x16& xb, int t, bool step, bool two) {
+  const float ta = max16_lean(xa);
+  const float tb = two ? max16_lean(xb) : -__builtin_inff();
+  const float tm = vmax2(ta, tb);
+  const bool better = step && tm > s.run_max;
+  const bool useb = tb > ta;
+  const uint64_t lanes = __builtin_amdgcn_ballot_w64(better);
+  const uint64_t ub = __builtin_amdgcn_ballot_w64(useb);
+  s.run_max = better ? tm : s.run_max;
+  s.best_tile = better ? t + (int)useb : s.best_tile;
+  sel_copy8<0>(s.best_val, xa, xb, lanes, ub);
+  sel_copy8<8>(s.best_val, xa, xb, lanes, ub);
+}
+
 // Leaner state: the running max and the absolute doc row that reached it
 // (lowest row on ties), resolved inside each tile as it is folded.
 struct RowState {

@@ -605,7 +605,11 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   };
   BlockState st[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) state_init(st[b], 0);
+  for (int b = 0; b < NB; ++b) {
+    state_init(st[b], 0);
+    Xa[b] = f32x16{};
+    Xb[b] = f32x16{};
+  }
   int cur = 0;                                   // stage of entry e
   // schedule words are read one step ahead, so no LDS round trip stands
   // between a step's start and its first load or MFMA
@@ -638,9 +642,10 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     gload(ld_meta, ld_unit, st_ld);
     if (ustart) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) state_init(st[b], t);
+      for (int b = 0; b < NB; ++b) state_begin(st[b], t);
     }
-    if (active && has) {
+    const bool step = active && has;
+    if (step) {
       const char* buf = lds + cur * kSTBytes;
       if (two) {
         if (word0 == kFull && word1 == kFull) {
@@ -652,24 +657,21 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
           tile_init(cb, word1, h);
           mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb);
         }
-        if constexpr (KEEP) {
-#pragma unroll
-          for (int b = 0; b < NB; ++b) state_fold_pair(st[b], Xa[b], Xb[b], t);
-        } else {
-#pragma unroll
-          for (int b = 0; b < NB; ++b)
-            st[b].run_max = __builtin_fmaxf(st[b].run_max,
-                                            __builtin_fmaxf(max16(Xa[b]), max16(Xb[b])));
-        }
       } else {
-        tile_mfma(Xa, buf, word0);
-        if constexpr (KEEP) {
+        tile_mfma(Xa, buf, word0);       // Xb keeps the previous step's values, unused
+      }
+    }
+    // One fold per step on every path, so the argmax state has a single
+    // definition in the loop and stays in its registers.  A step without
+    // tiles folds nothing; a single-tile step ignores Xb.
+    if constexpr (KEEP) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) state_fold_sparse(st[b], Xa[b], t);
-        } else {
+      for (int b = 0; b < NB; ++b) state_fold_step(st[b], Xa[b], Xb[b], t, step, two);
+    } else if (step) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) st[b].run_max = __builtin_fmaxf(st[b].run_max, max16(Xa[b]));
-        }
+      for (int b = 0; b < NB; ++b) {
+        const float tb = two ? max16_lean(Xb[b]) : -__builtin_inff();
+        st[b].run_max = vmax3(st[b].run_max, max16_lean(Xa[b]), tb);
       }
     }
     // entry e+1's rows (loaded one step ago) must be in LDS before the barrier
