@@ -152,7 +152,7 @@ lik_status forward_entry(int layout, const void* Q, const void* D, lik_dtype dty
   return ok();
 }
 
-constexpr int64_t kBwdMaxLd = 16000;   // one int per row in 64 KB of LDS
+constexpr int64_t kBwdMaxLd = 16000;   // workspace sort of grad_D: one int per row in 64 KB of LDS
 
 lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dtype,
                           int64_t nq_or_b, int64_t Lq, int64_t nd_or_n, int64_t Ld, int64_t dim,
@@ -173,11 +173,15 @@ lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dt
                 "Q, D, argmax, gradients and workspace must be 16-byte aligned");
   st = check_supported(dtype, s);
   if (st != LIK_OK) return st;
-  if (Ld > kBwdMaxLd)
-    return fail(LIK_ERR_UNSUPPORTED, "backward supports Ld <= %lld (got %lld)",
-                (long long)kBwdMaxLd, (long long)Ld);
   lik::BwdPlan p = lik::make_bwd_plan(layout, (int)dtype, nq_or_b, Lq, nd_or_n, Ld, dim,
                                       d_mask != nullptr, argmax != nullptr, q_mask != nullptr);
+  // only the workspace sort of grad_D keeps per-row tables in LDS; the fused
+  // all-pairs kernel sizes its own LDS and the pairwise/kd kernel streams rows
+  if (grad_D && p.gd_mode == lik::kGdSort && Ld > kBwdMaxLd)
+    return fail(LIK_ERR_UNSUPPORTED,
+                "backward with this shape sorts grad_D through the workspace, which supports "
+                "Ld <= %lld (got %lld)",
+                (long long)kBwdMaxLd, (long long)Ld);
   if (ws_bytes < p.total)
     return fail(LIK_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                 p.total);

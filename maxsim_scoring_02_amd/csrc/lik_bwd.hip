@@ -50,6 +50,7 @@ struct BwdArgs {
   int key_bits;
   int gq_slices;
   int fz_sw, fz_split;                      // fused grad_D: sorting waves, workgroups per doc
+  int gd_parts;                             // pairwise / kd grad_D: waves per document
   int fz_off_start, fz_off_cnt, fz_off_sorted, fz_off_gl, fz_off_union, fz_off_masks;  // LDS layout
   uint64_t lq_magic;                        // ceil(2^32 / Lq): h / Lq for h < 2^16
   int64_t Nq, Lq, n_docs, Ld, K, H;
@@ -843,7 +844,6 @@ template <> __device__ __forceinline__ void load4_as_float<Elem::F32>(const char
   f[3] = w.w;
 }
 
-constexpr int kGdPairsParts = 4;
 
 template <Elem E, int DIM>
 __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
@@ -853,16 +853,17 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
   constexpr int ES = ElemInfo<E>::kBytes;
   static_assert(F4 <= 64, "one gradient row per wave store at most");
   const int lane = threadIdx.x & 63;
-  // kGdPairsParts waves per document, each streaming a contiguous share of its
+  // gd_parts waves per document, each streaming a contiguous share of its
   // rows (whole stores of RPI rows), so enough stores are in flight
+  const int parts = a.gd_parts;
   const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t e = wv / kGdPairsParts;
-  const int part = (int)(wv - e * kGdPairsParts);
+  const int64_t e = wv / parts;
+  const int part = (int)(wv - e * parts);
   if (e >= a.n_docs) return;
   const int Lq = (int)a.Lq, Ld = (int)a.Ld;
   const int n_st = (Ld + RPI - 1) / RPI;                  // stores per document
-  const int r_begin = (int)((int64_t)n_st * part / kGdPairsParts) * RPI;
-  const int r_end = min((int)((int64_t)n_st * (part + 1) / kGdPairsParts) * RPI, Ld);
+  const int r_begin = (int)((int64_t)n_st * part / parts) * RPI;
+  const int r_end = min((int)((int64_t)n_st * (part + 1) / parts) * RPI, Ld);
   const int nh = (Lq + 63) / 64;
   const float g = a.g[e];
   const int64_t qbase = (e / a.K) * a.Lq;     // first Q row of this document's query
@@ -962,7 +963,7 @@ static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t fz_lds, hipStr
   }
   if (mode == kGdPairs) {
     hipLaunchKernelGGL((gradd_pairs_kernel<E, DIM>),
-                       dim3((unsigned)cdiv(a.n_docs * kGdPairsParts, 4)), dim3(256), 0, s, a);
+                       dim3((unsigned)cdiv(a.n_docs * a.gd_parts, 4)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   if (a.Ld <= kSortWavesMaxLd) {
@@ -1044,6 +1045,7 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
   a.gq_slices = p.gq_slices;
   a.fz_sw = p.fz_sw;
   a.fz_split = p.fz_split;
+  a.gd_parts = p.gd_parts;
   a.fz_off_start = p.fz_off_start;
   a.fz_off_cnt = p.fz_off_cnt;
   a.fz_off_sorted = p.fz_off_sorted;

@@ -48,8 +48,13 @@ struct FwdPlan {
 enum GdMode : int {
   kGdSort = 0,    // sort kernel + row kernel through the workspace (any shape)
   kGdFused = 1,   // all-pairs: one fused kernel per document, sort in LDS
-  kGdPairs = 2    // pairwise / kd: four waves per document stream its rows
+  kGdPairs = 2    // pairwise / kd: waves per document stream contiguous row ranges
 };
+// pairwise / kd grad_D: at least this many waves per document, and enough
+// over the batch to fill the chip (few long documents split finer)
+constexpr int kGdPairsMinParts = 4;
+constexpr int64_t kGdPairsWaves = 16384;
+constexpr int64_t kGdPairsMinRows = 64;   // rows a wave streams, at least
 constexpr int kFzThreads = 512;        // threads of the fused grad_D workgroup
 constexpr int kFzMaxHitsPerWave = 2048; // hits one sorting wave of it ranks
 constexpr int kPairsMaxLq = 256;   // longest query of the pairs grad_D kernel
@@ -61,6 +66,7 @@ struct BwdPlan {
   int64_t H = 0;            // hits per document (all-pairs Nq*Lq; pairs Lq)
   int key_bits = 1;
   int gd_mode = kGdSort;
+  int gd_parts = kGdPairsMinParts;   // pairwise / kd grad_D: waves per document
   // fused grad_D: sorting waves, workgroups per document, dynamic LDS layout
   int fz_sw = 0, fz_split = 1;
   int fz_off_start = 0, fz_off_cnt = 0, fz_off_sorted = 0, fz_off_gl = 0, fz_off_union = 0,
@@ -263,6 +269,11 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
     }
   } else if (layout != kAllPairs && Lq > 0 && Lq <= kPairsMaxLq && Ld > 0) {
     b.gd_mode = kGdPairs;
+    int64_t parts = cdiv(kGdPairsWaves, f.n_docs);
+    const int64_t by_rows = Ld / kGdPairsMinRows;
+    if (parts > by_rows) parts = by_rows;
+    if (parts < kGdPairsMinParts) parts = kGdPairsMinParts;
+    b.gd_parts = (int)parts;
   }
   // (rows of one slice are indexed with 32 bits)
   if (layout == kAllPairs && f.n_docs >= kGqSliceMinDocs && Lq > 0 && Ld > 0 &&

@@ -118,6 +118,22 @@ def test_backward_rejects_invalid_arguments(L):
     assert bwd(L, argmax=None, wsb=need - 1) == LIK_ERR_INVALID_ARG
     assert "workspace too small" in L.lik_last_error().decode()
     assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
+    assert "sorts grad_D through the workspace" in L.lik_last_error().decode()
+
+
+def test_long_pairwise_and_kd_backward_pass_the_row_limit(L):
+    # pairwise / kd stream grad_D rows, so Ld past the workspace sort's limit
+    # passes the row check; the calls then stop at the workspace check (no
+    # argmax given, so the forward is recomputed in a workspace that is too
+    # small), before any device work on any machine
+    st = L.lik_maxsim_pairwise_bwd(FAKE, FAKE, LIK_BF16, 2, 32, 40000, 128, None, None, FAKE,
+                                   None, FAKE, FAKE, FAKE, 1, None)
+    assert st == LIK_ERR_INVALID_ARG
+    assert "workspace too small" in L.lik_last_error().decode()
+    st = L.lik_maxsim_kd_bwd(FAKE, FAKE, LIK_BF16, 2, 32, 3, 40000, 128, None, None, FAKE,
+                             None, FAKE, FAKE, FAKE, 1, None)
+    assert st == LIK_ERR_INVALID_ARG
+    assert "workspace too small" in L.lik_last_error().decode()
 
 
 def test_zero_sized_calls_are_ok_noops(L):

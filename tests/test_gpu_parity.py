@@ -14,7 +14,8 @@ import torch
 import oracle
 from maxsim_scoring_02_amd import workloads as wl
 from maxsim_scoring_02_amd.workloads import Workload
-from parity import ORACLE_FWD, check_scores, full_check, gpu_backward, gpu_forward, say
+from parity import (ORACLE_BWD, ORACLE_FWD, check_argmax, check_grads, check_scores, full_check,
+                    gpu_backward, gpu_forward, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +67,68 @@ def test_long_docs_reduced_split_chunks():
 def test_long_rerank_reduced_split():
     w = wl.long_rerank(B=3, Ld=32768)
     full_check(w, backward=False)
+
+
+# ------------------------------------------------- long-context backward
+
+def test_long_docs_backward_masked_tails():
+    """All-pairs backward at Ld = 8192 with masked tails of every length."""
+    w = wl.long_docs(Nq=5, Nd=6, Ld=8192)
+    g = wl.gaussian_grad(7005, (5, 6)).numpy()
+    full_check(w, grad=g)
+
+
+def test_long_rerank_backward_reduced():
+    """Pairwise backward at Ld = 32768 (streamed grad_D, no row tables)."""
+    w = wl.long_rerank(B=3, Ld=32768)
+    g = wl.gaussian_grad(7006, (3,)).numpy()
+    full_check(w, grad=g)
+
+
+def test_kd_backward_past_the_sort_limit():
+    """kd backward with Ld = 20000, above the workspace sort's row limit."""
+    rng = np.random.default_rng(7007)
+    Q = _rand_tokens(rng, (2, 32, 128))
+    D = _rand_tokens(rng, (2, 3, 20000, 128))
+    dm = np.ones((2, 3, 20000), dtype=bool)
+    dm[0, 1, 12345:] = False
+    dm[1, 2, :19000] = False
+    g = rng.standard_normal((2, 3))
+    full_check(_custom("kd-ld20000", "kd", "f16", Q, D, None, dm, g))
+
+
+def _sub_pairwise(w, idx):
+    return Workload(f"{w.name}-sample", "pairwise", w.dtype, w.Q[idx].contiguous(),
+                    w.D[idx].contiguous(), None, None, None)
+
+
+def test_long_rerank_backward_full_size_sampled():
+    """The full long-rerank shape (64 pairs x 32768 tokens) in the launch
+    configuration of the full batch: sampled pairs against the oracle, the
+    Euler identity over the whole batch, and the recomputed-argmax backward
+    bitwise equal to the one given the forward's argmax."""
+    w = wl.long_rerank()
+    B = w.Q.shape[0]
+    g = wl.gaussian_grad(7008, (B,)).numpy()
+    s, a = gpu_forward(w)
+    gQ, gD = gpu_backward(w, g, a)
+    idx = [0, 17, B - 1]
+    sub = _sub_pairwise(w, idx)
+    Qn, Dn, _, _ = sub.numpy_inputs()
+    ref = ORACLE_FWD["pairwise"](Qn, Dn, None, None)
+    check_scores(s[idx], ref)
+    merged = check_argmax(a[idx], ref, sub)
+    rQ, rD = ORACLE_BWD["pairwise"](Qn, Dn, g[idx].astype(np.float64), merged, None, None)
+    check_grads(gQ[idx], rQ, "grad_Q")
+    check_grads(gD[idx], rD, "grad_D")
+    # Euler identity (the score is 1-homogeneous in Q and in D)
+    rhs = float(np.sum(g.astype(np.float64) * s))
+    lq = float(np.sum(w.Q.double().numpy() * gQ))
+    ld = float(torch.sum(w.D.double() * torch.from_numpy(gD).double()))
+    assert abs(lq - rhs) <= 1e-4 * max(1.0, abs(rhs))
+    assert abs(ld - rhs) <= 1e-4 * max(1.0, abs(rhs))
+    gQ2, gD2 = gpu_backward(w, g, None)
+    assert np.array_equal(gQ, gQ2) and np.array_equal(gD, gD2)
 
 
 # ------------------------------------------------------------- shape sweep

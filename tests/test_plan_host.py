@@ -14,7 +14,10 @@ checking it themselves:
 - a query mask switches all-pairs to compacted token slots: split path,
   slots for every token, token tables inside the workspace;
 - fused grad_D: its LDS layout fits the size the plan reports and each
-  sorting wave ranks at most the hits it can hold.
+  sorting wave ranks at most the hits it can hold;
+- pairwise / kd grad_D: waves per document at least the minimum, split
+  finer only when the batch is too small to fill the chip, never below the
+  minimum rows per wave, and the grid fits.
 
 The numeric constants the kernels use (64 units, 32 entries per unit, 256
 threads, 8 sort-wave slots) are restated here as the kernels' own limits.
@@ -108,6 +111,18 @@ static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     CHECK((size_t)b.fz_off_masks + (size_t)b.fz_sw * Ld * 8 <= b.fz_lds, "masks inside LDS");
     CHECK(b.fz_lds <= 160 * 1024, "LDS %zu", b.fz_lds);
   }
+  if (b.gd_mode == kGdPairs) {
+    // waves per document: at least the minimum, never more than the rows
+    // allow beyond it, and the launch (4 waves per workgroup) fits the grid
+    CHECK(layout != kAllPairs && Lq <= kPairsMaxLq, "pairs grad_D only for pairwise / kd");
+    CHECK(b.gd_parts >= kGdPairsMinParts, "parts %d", b.gd_parts);
+    CHECK(b.gd_parts == kGdPairsMinParts || (long)b.gd_parts * kGdPairsMinRows <= Ld,
+          "parts %d for Ld %ld", b.gd_parts, Ld);
+    CHECK(b.fwd.n_docs * b.gd_parts >= kGdPairsWaves || b.gd_parts == kGdPairsMinParts ||
+              (long)b.gd_parts == Ld / kGdPairsMinRows,
+          "parts %d do not fill the chip", b.gd_parts);
+    CHECK((b.fwd.n_docs * b.gd_parts + 3) / 4 < (1L << 31), "grid");
+  }
   CHECK(b.total >= b.fwd.fwd_bytes || !b.recompute, "bwd total");
 }
 
@@ -128,6 +143,8 @@ int main() {
               fwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim, true);
               fwd_case(kKd, elem, Nq, Lq, 16, Ld, dim, false);
               if (Ld <= 16000) bwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim);
+              bwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim);
+              bwd_case(kKd, elem, Nq, Lq, Nd % 32 + 1, Ld, dim);
             }
   std::printf("fails %d\n", fails);
   return fails ? 1 : 0;
