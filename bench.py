@@ -21,7 +21,9 @@ Throughput counts algorithmic work on valid tokens only:
 (one gathered row-FMA for grad_Q and one scattered row-FMA for grad_D).
 
 Other workloads (--workload): inbatch-pages, kd-candidates, long-docs,
-long-rerank, or `all` (one line each).  Memory-bound workloads report GB/s of
+long-rerank, or `all` (one line each); `next` runs the long-context backward
+(long-docs-bwd, long-rerank-bwd: the long-document inputs with a Gaussian
+upstream grad, forward + backward).  Memory-bound workloads report GB/s of
 compulsory traffic (inputs' valid rows read once, outputs and float32
 gradients written once).
 
@@ -243,6 +245,18 @@ def make_workload(name: str):
         return wl.long_docs(), False
     if name == "long-rerank":
         return wl.long_rerank(), False
+    # the long-context backward (the step after the long-document forward):
+    # the same inputs with a Gaussian upstream grad, forward + backward
+    if name == "long-docs-bwd":
+        w = wl.long_docs()
+        w.grad = wl.gaussian_grad(2005, (w.Q.shape[0], w.D.shape[0]))
+        w.name = name
+        return w, True
+    if name == "long-rerank-bwd":
+        w = wl.long_rerank()
+        w.grad = wl.gaussian_grad(2006, (w.Q.shape[0],))
+        w.name = name
+        return w, True
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -252,6 +266,8 @@ DOMINANT = {  # kernel whose roofline is reported, and its bound
     "long-docs": ("allpairs_fwd", "mfma"),
     "kd-candidates": ("pairs_fwd", "hbm"),
     "long-rerank": ("pairs_fwd", "hbm"),
+    "long-docs-bwd": ("allpairs_fwd", "mfma"),
+    "long-rerank-bwd": ("pairs_fwd", "hbm"),
 }
 
 
@@ -518,8 +534,9 @@ def main():
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, max(args.steps, 1))
         return
-    names = (["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"]
-             if args.workload == "all" else [args.workload])
+    groups = {"all": ["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"],
+              "next": ["long-docs-bwd", "long-rerank-bwd"]}
+    names = groups.get(args.workload, [args.workload])
     for i, name in enumerate(names):
         line = bench_one(name, args.steps, args.warmup,
                          with_cpu=(not args.no_cpu_baseline))
