@@ -21,6 +21,8 @@ Modules:
   kd (per-query candidate) layouts, with tie information for parity checks.
 * ``brute``   pure-Python loops with ``math.fsum``, for tiny inputs only; it
   pins ``maxsim`` independently of numpy's matmul.
+* ``loss``    float64 row cross-entropy over a score matrix (the loss head
+  the colpali pull request puts on the scores), with its gradient.
 
 Every function here is pinned by the ``-m "not gpu"`` tests (brute force,
 closed forms, finite differences, invariants, integer-exact inputs); none is
@@ -42,4 +44,5 @@ from .maxsim import (  # noqa: F401
     maxsim_block,
     scores_as_float32,
 )
+from .loss import ce_rows  # noqa: F401
 from . import brute  # noqa: F401

@@ -425,3 +425,80 @@ def test_block_helper_matches_layouts():
     r = oracle.maxsim_allpairs(Q, D, qm, dm)
     s, a, gp = maxsim_block(Q, qm, D[1], dm[1])
     assert np.array_equal(s, r.scores[:, 1]) and np.array_equal(a, r.argmax[:, 1])
+
+
+# ---------------------------------------------------------------- loss head
+# oracle.ce_rows: softmax cross-entropy per score row, one target per row,
+# mean over rows (the reading of the colpali PR's in-batch and negative-doc
+# losses).  Pinned by closed forms, a pure-Python version and finite
+# differences.
+
+def _ce_brute(S, labels, scale):
+    """math.exp / math.log / math.fsum, row by row, no numpy arithmetic."""
+    R, C = len(S), len(S[0])
+    rows, grad = [], []
+    for r in range(R):
+        z = [scale * float(S[r][c]) for c in range(C)]
+        m = max(z)
+        tot = math.fsum(math.exp(x - m) for x in z)
+        lse = m + math.log(tot)
+        rows.append(lse - z[labels[r]])
+        grad.append([scale / R * (math.exp(z[c] - lse) - (1.0 if c == labels[r] else 0.0))
+                     for c in range(C)])
+    return math.fsum(rows) / R, rows, grad
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.05, 20.0])
+def test_ce_rows_matches_pure_python(scale):
+    rng = _rng(41)
+    S = rng.standard_normal((5, 7)) * 10
+    labels = rng.integers(0, 7, size=5)
+    loss, rows, grad = oracle.ce_rows(S, labels, scale)
+    bl, brows, bgrad = _ce_brute(S.tolist(), labels.tolist(), scale)
+    assert abs(loss - bl) <= 1e-12 * max(1.0, abs(bl))
+    assert np.allclose(rows, brows, rtol=1e-12, atol=1e-12)
+    assert np.allclose(grad, np.array(bgrad), rtol=1e-12, atol=1e-15)
+    # the diagonal default is labels = arange(R)
+    sq = S[:, :5]
+    assert oracle.ce_rows(sq)[0] == oracle.ce_rows(sq, np.arange(5))[0]
+
+
+def test_ce_rows_closed_forms():
+    # equal scores in a row: every class has probability 1/C, loss log C,
+    # gradient (1/C - [c == t]) * s / R
+    R, C = 3, 8
+    S = np.full((R, C), 4.25)
+    loss, rows, grad = oracle.ce_rows(S, np.array([0, 3, 7]), 2.0)
+    assert np.allclose(rows, math.log(C), atol=1e-14)
+    expect = np.full((R, C), 2.0 / R / C)
+    expect[[0, 1, 2], [0, 3, 7]] -= 2.0 / R
+    assert np.allclose(grad, expect, atol=1e-15)
+    # two classes: the loss is the softplus of the margin
+    S2 = np.array([[1.5, -2.0], [0.25, 3.0]])
+    _, rows2, grad2 = oracle.ce_rows(S2, np.array([0, 0]))
+    for r in range(2):
+        margin = S2[r, 1] - S2[r, 0]
+        assert abs(rows2[r] - math.log1p(math.exp(margin))) <= 1e-14
+        assert abs(grad2[r, 1] - 0.5 / (1 + math.exp(-margin))) <= 1e-15
+    # large logits stay finite (the row maximum is subtracted first)
+    big = np.array([[1000.0, 0.0, -1000.0]])
+    l3, _, g3 = oracle.ce_rows(big, np.array([1]))
+    assert abs(l3 - 1000.0) <= 1e-9 and np.isfinite(g3).all()
+
+
+def test_ce_rows_gradient_by_finite_differences_and_invariants():
+    rng = _rng(43)
+    S = rng.standard_normal((4, 6)) * 3
+    labels = np.array([5, 0, 2, 2])
+    loss, rows, grad = oracle.ce_rows(S, labels, 1.7)
+    h = 1e-6
+    for r in range(4):
+        for c in range(6):
+            P = S.copy(); P[r, c] += h
+            M = S.copy(); M[r, c] -= h
+            fd = (oracle.ce_rows(P, labels, 1.7)[0] - oracle.ce_rows(M, labels, 1.7)[0]) / (2 * h)
+            assert abs(fd - grad[r, c]) <= 1e-8
+    # each gradient row sums to zero; shifting a row leaves the loss unchanged
+    assert np.allclose(grad.sum(axis=1), 0.0, atol=1e-15)
+    shifted = S + np.array([[3.0], [-7.0], [0.5], [100.0]])
+    assert abs(oracle.ce_rows(shifted, labels, 1.7)[0] - loss) <= 1e-12
