@@ -23,7 +23,12 @@ Throughput counts algorithmic work on valid tokens only:
 Other workloads (--workload): inbatch-pages, kd-candidates, long-docs,
 long-rerank, or `all` (one line each); `next` runs the long-context backward
 (long-docs-bwd, long-rerank-bwd: the long-document inputs with a Gaussian
-upstream grad, forward + backward).  Memory-bound workloads report GB/s of
+upstream grad, forward + backward) and kd-loss-head (the kd-candidates
+inputs with the negative-doc cross-entropy as the loss head).
+
+In-batch pages and kd-loss-head steps run the loss head on the GPU between
+forward and backward (cross-entropy over the score rows, library entry
+lik_ce_rows); its time is part of the step and of `config.bwd_ms`.  Memory-bound workloads report GB/s of
 compulsory traffic (inputs' valid rows read once, outputs and float32
 gradients written once).
 
@@ -147,6 +152,15 @@ class Op:
         mk = lambda n: torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         self.wsf = mk(self.wsf_n)
         self.wsb = mk(self.wsb_n)
+        # loss head (cross-entropy over the score rows) run by bwd() first:
+        # "diag" targets the diagonal, "label0" candidate 0
+        self.loss_head = w.meta.get("loss_head") if backward else None
+        if self.loss_head:
+            R, C = shape
+            self.row_loss = torch.empty((R,), dtype=torch.float32, device=dev)
+            self.loss = torch.empty((1,), dtype=torch.float32, device=dev)
+            self.labels = (torch.zeros((R,), dtype=torch.int32, device=dev)
+                           if self.loss_head == "label0" else None)
         if backward:
             g = w.grad if w.grad is not None else None
             self.g = (g.to(dev).contiguous() if g is not None
@@ -181,6 +195,12 @@ class Op:
     def bwd(self):
         p, L = self.p, self.L
         Nq, Lq, Nx, Ld, dim = self.dims
+        if self.loss_head:
+            R, C = self.scores.shape
+            st = L.lik_ce_rows(p(self.scores), R, C, p(self.labels), 1.0, p(self.row_loss),
+                               p(self.loss), p(self.g), self.stream())
+            if st != 0:
+                raise RuntimeError(f"loss head failed: {L.lik_last_error().decode()}")
         args = (p(self.qm), p(self.dm), p(self.g), p(self.argmax), p(self.gQ), p(self.gD),
                 p(self.wsb), self.wsb_n, self.stream())
         if self.lay == "allpairs":
@@ -231,13 +251,18 @@ def make_workload(name: str):
         return wl.inbatch_text(), True
     if name == "inbatch-pages":
         w = wl.inbatch_pages()
-        # upstream grad of the cross-entropy over the diagonal, from the
-        # scores of the forward itself (formed once, outside the timed steps)
-        import torch
-        op = Op(w, backward=False)
-        op.fwd()
-        torch.cuda.synchronize()
-        w.grad = torch.from_numpy(wl.ce_diag_grad(op.scores.cpu().numpy()))
+        # the upstream grad is the loss head's: cross-entropy over the
+        # diagonal of the step's own scores, on the GPU inside every step
+        w.meta["loss_head"] = "diag"
+        return w, True
+    if name == "kd-loss-head":
+        # the pages' loss-head benchmark shape (B 256 x 16 candidates, Lq 32,
+        # Ld 1030): kd forward, negative-doc cross-entropy with candidate 0
+        # as the target, backward
+        w = wl.kd_candidates()
+        w.name = name
+        w.grad = None
+        w.meta["loss_head"] = "label0"
         return w, True
     if name == "kd-candidates":
         return wl.kd_candidates(), True
@@ -268,6 +293,7 @@ DOMINANT = {  # kernel whose roofline is reported, and its bound
     "long-rerank": ("pairs_fwd", "hbm"),
     "long-docs-bwd": ("allpairs_fwd", "mfma"),
     "long-rerank-bwd": ("pairs_fwd", "hbm"),
+    "kd-loss-head": ("pairs_fwd", "hbm"),
 }
 
 
@@ -310,6 +336,10 @@ def cpu_baseline(w, backward: bool, budget_s: float = 12.0):
         t0 = time.perf_counter()
         r = fw(Qs, Ds, qms, dms)
         if backward:
+            head = w.meta.get("loss_head")
+            if head:
+                labels = None if head == "diag" else np.zeros(k, dtype=np.int64)
+                gs = oracle.ce_rows(r.scores, labels)[2]
             bw(Qs, Ds, gs, r.argmax, qms, dms)
         dt = time.perf_counter() - t0
         import torch
@@ -535,7 +565,7 @@ def main():
         copy_calibration(args.copy_calibration, max(args.steps, 1))
         return
     groups = {"all": ["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"],
-              "next": ["long-docs-bwd", "long-rerank-bwd"]}
+              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head"]}
     names = groups.get(args.workload, [args.workload])
     for i, name in enumerate(names):
         line = bench_one(name, args.steps, args.warmup,

@@ -210,6 +210,38 @@ lik_status lik_maxsim_kd_bwd(const void* Q, const void* D, lik_dtype dtype,
                              float* grad_D, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Loss head: softmax cross-entropy over the rows of a score matrix.
+ *
+ * The colpali pull request ("What this PR adds") routes its in-batch ColBERT
+ * loss and its negative-doc losses (over kd scores) through MaxSim, and its
+ * "Results" benchmark this loss head together with the operator.  The pages
+ * do not define the losses; the reading implemented is the row
+ * cross-entropy with one target column t_r per row, mean over rows, logits
+ * scaled by `scale`:
+ *   row_loss[r] = logsumexp_c(scale*S[r,c]) - scale*S[r,t_r]
+ *   *loss       = mean_r row_loss[r]
+ *   grad[r,c]   = scale/R * (softmax_c(scale*S[r,:]) - [c == t_r])
+ * In-batch loss: labels NULL (t_r = r, needs C >= R).  Negative-doc loss over
+ * kd scores [B, N] with the positive as candidate 0: labels all 0.
+ *
+ * scores      [R, C] float32, row-major, device.
+ * labels      [R] int32 target columns, device, or NULL for the diagonal.
+ *             A label outside [0, C) makes that row's loss NaN (so the mean
+ *             is NaN) and leaves the -1 term out of its gradient row.
+ * scale       logit multiplier, finite and non-zero (1 = no temperature).
+ * row_loss    [R] float32 output, device (also the reduction buffer).
+ * loss        [1] float32 output, device: the mean, summed in a fixed order
+ *             in float64, so bitwise reproducible.
+ * grad_scores [R, C] float32 output (overwritten), or NULL to skip; it is the
+ *             grad_scores input of the backward entry points.
+ * R == 0 is a successful no-op.  Pointers 4-byte aligned.  Asynchronous on
+ * `stream`; nothing is allocated.
+ * ------------------------------------------------------------------------ */
+lik_status lik_ce_rows(const float* scores, int64_t R, int64_t C,
+                       const int32_t* labels, float scale, float* row_loss,
+                       float* loss, float* grad_scores, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

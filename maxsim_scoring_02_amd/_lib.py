@@ -53,6 +53,7 @@ SIGNATURES = {
     "lik_maxsim_pairwise_bwd": (_BWD_PAIRWISE, _I),
     "lik_maxsim_kd_fwd": (_FWD_ALLPAIRS, _I),
     "lik_maxsim_kd_bwd": (_BWD_ALLPAIRS, _I),
+    "lik_ce_rows": ([_P, _I64, _I64, _P, ctypes.c_float, _P, _P, _P, _P], _I),
 }
 
 
@@ -270,6 +271,27 @@ def lik_maxsim_kd_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
                                    _ptr(g), _ptr(am), _ptr(gQ), _ptr(gD), _ptr(ws), wsb,
                                    _stream()))
     return gQ, gD
+
+
+def lik_ce_rows(scores, labels=None, scale=1.0, want_grad=True) -> Tuple:
+    """Loss head: row cross-entropy of float32 scores [R, C] with targets
+    `labels` [R] (int32) or the diagonal (None).  Returns (loss [1],
+    row_loss [R], grad [R, C] or None), all float32 on the scores' device."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or not scores.is_cuda:
+        raise ValueError("scores must be a 2-D float32 CUDA tensor")
+    S = scores.contiguous()
+    R, C = S.shape
+    lab = None
+    if labels is not None:
+        lab = labels.to(device=S.device, dtype=torch.int32).contiguous()
+        if tuple(lab.shape) != (R,):
+            raise ValueError(f"labels must have shape ({R},)")
+    row_loss = torch.empty((R,), dtype=torch.float32, device=S.device)
+    loss = torch.empty((1,), dtype=torch.float32, device=S.device)
+    grad = torch.empty((R, C), dtype=torch.float32, device=S.device) if want_grad else None
+    _check(lib().lik_ce_rows(_ptr(S), R, C, _ptr(lab), float(scale), _ptr(row_loss), _ptr(loss),
+                             _ptr(grad), _stream()))
+    return loss, row_loss, grad
 
 
 FORWARD = {"allpairs": lik_maxsim_fwd, "pairwise": lik_maxsim_pairwise_fwd,

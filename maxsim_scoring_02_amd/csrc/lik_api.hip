@@ -310,4 +310,32 @@ lik_status lik_maxsim_kd_bwd(const void* Q, const void* D, lik_dtype dtype, int6
                         argmax, grad_Q, grad_D, workspace, workspace_bytes, stream);
 }
 
+lik_status lik_ce_rows(const float* scores, int64_t R, int64_t C, const int32_t* labels,
+                       float scale, float* row_loss, float* loss, float* grad_scores,
+                       void* stream) {
+  if (R < 0 || C < 0) return fail(LIK_ERR_INVALID_ARG, "negative size (R %lld, C %lld)",
+                                  (long long)R, (long long)C);
+  if (mul_ok({R, C}) < 0) return fail(LIK_ERR_INVALID_ARG, "R x C overflows");
+  if (R == 0) return ok();
+  if (C == 0) return fail(LIK_ERR_INVALID_ARG, "rows have no columns (C == 0)");
+  if (!labels && C < R)
+    return fail(LIK_ERR_INVALID_ARG, "diagonal targets need C >= R (got R %lld, C %lld)",
+                (long long)R, (long long)C);
+  if (!scores) return fail(LIK_ERR_INVALID_ARG, "scores is NULL");
+  if (!row_loss) return fail(LIK_ERR_INVALID_ARG, "row_loss is NULL");
+  if (!loss) return fail(LIK_ERR_INVALID_ARG, "loss is NULL");
+  if (!(scale == scale) || scale == 0.0f || scale > 3.4e38f || scale < -3.4e38f)
+    return fail(LIK_ERR_INVALID_ARG, "scale must be finite and non-zero");
+  if (!aligned4(scores) || !aligned4(labels) || !aligned4(row_loss) || !aligned4(loss) ||
+      !aligned4(grad_scores))
+    return fail(LIK_ERR_INVALID_ARG, "scores, labels, losses and gradient must be 4-byte aligned");
+  if (R > (int64_t(1) << 32)) return fail(LIK_ERR_UNSUPPORTED, "R > 2^32 rows");
+  lik_status st = check_device();
+  if (st != LIK_OK) return st;
+  hipError_t e = lik::run_ce_rows(scores, R, C, labels, scale, row_loss, loss, grad_scores,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(LIK_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

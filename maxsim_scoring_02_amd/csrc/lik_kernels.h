@@ -47,4 +47,8 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
                         const uint8_t* d_mask, const float* grad_scores, const int32_t* argmax,
                         float* grad_Q, float* grad_D, char* ws, hipStream_t s);
 
+// Loss head: row cross-entropy of a score matrix (lik_loss.hip).
+hipError_t run_ce_rows(const float* S, int64_t R, int64_t C, const int32_t* labels, float scale,
+                       float* row_loss, float* loss, float* grad, hipStream_t s);
+
 }  // namespace lik

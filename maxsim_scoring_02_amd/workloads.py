@@ -166,9 +166,9 @@ def inbatch_pages(seed: int = 1003, B: int = 128, Lq: int = 32, Ld: int = 1030,
                   dim: int = 128, dtype: str = "bf16", q_lo: int = 8,
                   q_hi: int = 32) -> Workload:
     """ColPali-scale in-batch contrastive: query lengths uniform in
-    [q_lo, q_hi] (zero, masked tail), docs all valid.  The upstream grad is a
-    cross-entropy over the diagonal of the scores, so it is left None here and
-    formed by the caller from a score matrix (see ``ce_diag_grad``)."""
+    [q_lo, q_hi] (zero, masked tail), docs all valid.  The upstream grad is
+    the gradient of a cross-entropy over the diagonal of the scores, so it is
+    left None here: the loss head forms it from the scores."""
     rng = np.random.default_rng(seed)
     Q = _normalize_round(rng.standard_normal((B, Lq, dim), dtype=np.float32), dtype)
     D = _normalize_round(rng.standard_normal((B, Ld, dim), dtype=np.float32), dtype)
@@ -236,24 +236,3 @@ def gaussian_grad(seed: int, shape) -> torch.Tensor:
     """A separate seeded N(0,1) float32 upstream grad."""
     return torch.from_numpy(
         np.random.default_rng(seed).standard_normal(shape, dtype=np.float32))
-
-
-def ce_diag_grad(scores: np.ndarray) -> np.ndarray:
-    """Upstream grad of a mean cross-entropy over rows with the diagonal as
-    the target class (labels = arange(B), no temperature):
-    g = (softmax_row(scores) - I) / B, in float32.  This is the training loss
-    wrapped around the scores, not part of the scoring operator."""
-    s = np.asarray(scores, dtype=np.float64)
-    s = s - s.max(axis=1, keepdims=True)
-    p = np.exp(s)
-    p /= p.sum(axis=1, keepdims=True)
-    B = s.shape[0]
-    p[np.arange(B), np.arange(B)] -= 1.0
-    return (p / B).astype(np.float32)
-
-
-def ce_diag_loss(scores: np.ndarray) -> float:
-    s = np.asarray(scores, dtype=np.float64)
-    m = s.max(axis=1, keepdims=True)
-    lse = (m[:, 0] + np.log(np.exp(s - m).sum(axis=1)))
-    return float(np.mean(lse - np.diag(s)))

@@ -26,7 +26,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = _lib.header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), f"liblik.so does not export {n}"
     assert set(names) == set(_lib.SIGNATURES)
@@ -179,3 +179,29 @@ def test_device_check_without_a_gpu(L):
     need = L.lik_workspace_bytes(LIK_OP_FWD, 2, 32, 3, 40, 128, LIK_BF16, 0)
     assert fwd(L, wsb=need) == LIK_ERR_UNSUPPORTED
     assert "device" in L.lik_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(R=-1), "negative"),
+    (dict(C=0), "no columns"),
+    (dict(labels=None, R=5, C=4), "diagonal"),
+    (dict(scores=None), "scores is NULL"),
+    (dict(row_loss=None), "row_loss is NULL"),
+    (dict(loss=None), "loss is NULL"),
+    (dict(scale=0.0), "scale"),
+    (dict(scale=float("nan")), "scale"),
+    (dict(scale=float("inf")), "scale"),
+    (dict(scores=P(0x1002)), "aligned"),
+])
+def test_loss_head_rejects_invalid_arguments(L, kw, msg):
+    a = dict(scores=FAKE, R=4, C=4, labels=FAKE, scale=1.0, row_loss=FAKE, loss=FAKE,
+             grad=FAKE, stream=None)
+    a.update(kw)
+    st = L.lik_ce_rows(a["scores"], a["R"], a["C"], a["labels"], a["scale"], a["row_loss"],
+                       a["loss"], a["grad"], a["stream"])
+    assert st == LIK_ERR_INVALID_ARG
+    assert msg in L.lik_last_error().decode()
+
+
+def test_loss_head_zero_rows_is_a_noop(L):
+    assert L.lik_ce_rows(None, 0, 7, None, 1.0, None, None, None, None) == 0
