@@ -217,10 +217,15 @@ class Op:
 # measured HBM traffic recorded from rocprofv3 counters
 # --------------------------------------------------------------------------
 
+# the sources the forward kernels (the ones whose traffic is recorded) and
+# their launch plans are built from
+FORWARD_SOURCES = ("lik_device.h", "lik_fwd.hip", "lik_kernels.h", "lik_plan.h")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "maxsim_scoring_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FORWARD_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
