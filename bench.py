@@ -20,6 +20,11 @@ Throughput counts algorithmic work on valid tokens only:
   backward  4 * dim * (valid (q, i, d) triples with d non-empty)
 (one gathered row-FMA for grad_Q and one scattered row-FMA for grad_D).
 
+Memory-bound workloads count bytes of compulsory traffic over the step:
+every valid input row read once, masks, scores and the kept argmax written,
+and for the backward the upstream grad and argmax read and the float32
+gradients written.
+
 Other workloads (--workload): inbatch-pages, kd-candidates, long-docs,
 long-rerank, or `all` (one line each); `next` runs the long-context backward
 (long-docs-bwd, long-rerank-bwd: the long-document inputs with a Gaussian
@@ -28,9 +33,7 @@ inputs with the negative-doc cross-entropy as the loss head).
 
 In-batch pages and kd-loss-head steps run the loss head on the GPU between
 forward and backward (cross-entropy over the score rows, library entry
-lik_ce_rows); its time is part of the step and of `config.bwd_ms`.  Memory-bound workloads report GB/s of
-compulsory traffic (inputs' valid rows read once, outputs and float32
-gradients written once).
+lik_ce_rows); its time is part of the step and of `config.bwd_ms`.
 
 `cpu_baseline` is the CPU oracle timed on this machine's cores on a bounded
 sample of the same workload (the sample is named in the JSON).
@@ -102,8 +105,11 @@ def work(w, keep_argmax=True):
     mask_bytes = (0 if w.q_mask is None else w.q_mask.numel()) + \
                  (0 if w.d_mask is None else w.d_mask.numel())
     b_fwd = q_bytes + d_bytes + mask_bytes + n_scores * 4 + (n_scores * Lq * 4 if keep_argmax else 0)
+    # over a step every input row counts once (in the forward's bytes): the
+    # backward adds the upstream grad and argmax it reads and the float32
+    # gradients it writes
     d_rows = float(np.prod(w.D.shape[:-1]))
-    b_bwd = (q_bytes + d_bytes + n_scores * 4 + n_scores * Lq * 4
+    b_bwd = (n_scores * 4 + n_scores * Lq * 4
              + w.Q.shape[0] * Lq * dim * 4 + d_rows * dim * 4)
     return f_fwd, f_bwd, b_fwd, b_bwd
 
