@@ -19,6 +19,9 @@ checking it themselves:
   finer only when the batch is too small to fill the chip, never below the
   minimum rows per wave, and the grid fits.
 
+A second test pins the benchmark's work accounting (valid-token flops;
+bytes with every input row counted once per step) to hand-written sums.
+
 The numeric constants the kernels use (64 units, 32 entries per unit, 256
 threads, 8 sort-wave slots) are restated here as the kernels' own limits.
 """
@@ -161,3 +164,36 @@ def test_launch_plan_invariants(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-2000:]
     assert "fails 0" in r.stdout
+
+
+def test_bench_work_accounting():
+    """bench.work on a tiny all-pairs and a kd workload, against sums written
+    out by hand: valid-token flops, and each input row counted once per step
+    (in the forward's bytes)."""
+    import sys
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import bench
+    from maxsim_scoring_02_amd.workloads import Workload
+
+    Q = torch.zeros((2, 3, 64), dtype=torch.bfloat16)
+    D = torch.zeros((4, 5, 64), dtype=torch.bfloat16)
+    qm = torch.tensor([[1, 1, 0], [1, 0, 0]], dtype=torch.bool)
+    dm = torch.tensor([[1] * 5, [1, 1, 0, 0, 0], [0] * 5, [1, 0, 1, 0, 1]], dtype=torch.bool)
+    w = Workload("t", "allpairs", "bf16", Q, D, qm, dm, None)
+    f_fwd, f_bwd, b_fwd, b_bwd = bench.work(w)
+    qv, dv = np.array([2, 1]), np.array([5, 2, 0, 3])
+    assert f_fwd == 2 * 64 * qv.sum() * dv.sum()
+    assert f_bwd == 4 * 64 * qv.sum() * 3                 # three non-empty documents
+    pairs = 2 * 4
+    assert b_fwd == (qv.sum() + dv.sum()) * 64 * 2 + qm.numel() + dm.numel() + pairs * 4 + pairs * 3 * 4
+    assert b_bwd == pairs * 4 + pairs * 3 * 4 + 2 * 3 * 64 * 4 + 4 * 5 * 64 * 4
+    # kd: B=2 queries with N=3 candidates of 7 tokens, no masks
+    wk = Workload("k", "kd", "f16", torch.zeros((2, 4, 64), dtype=torch.float16),
+                  torch.zeros((2, 3, 7, 64), dtype=torch.float16), None, None, None)
+    f_fwd, f_bwd, b_fwd, b_bwd = bench.work(wk, keep_argmax=False)
+    assert f_fwd == 2 * 64 * 4 * 7 * 6 and f_bwd == 4 * 64 * 4 * 6
+    assert b_fwd == (2 * 4 + 6 * 7) * 64 * 2 + 6 * 4
