@@ -878,34 +878,48 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
   const int sub = lane / F4, f = lane - (lane / F4) * F4;
   float* out = a.gD + e * (int64_t)Ld * DIM;
   const char* Qb = (const char*)a.Q;
-  for (int r0 = r_begin; r0 < r_end; r0 += RPI) {
+  // U stores (U * RPI rows) per hit check, so several stores are in flight
+  // and the check is paid once for them; each row is still written once,
+  // with its hits added in increasing h
+  constexpr int U = 4;
+  for (int r0 = r_begin; r0 < r_end; r0 += RPI * U) {
     bool any = false;
 #pragma unroll
-    for (int k = 0; k < NH; ++k) any |= (k < nh) && key[k] >= r0 && key[k] < r0 + RPI;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NH; ++k) any |= (k < nh) && key[k] >= r0 && key[k] < r0 + RPI * U;
+    float v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[u][t] = 0.f;
     if (__ballot(any) != 0ull) {
-      for (int rr = 0; rr < RPI; ++rr) {
 #pragma unroll
-        for (int k = 0; k < NH; ++k) {
-          if (k >= nh) break;
-          uint64_t m = __ballot(key[k] == r0 + rr);
-          while (m != 0ull) {
-            const int b = __ffsll((unsigned long long)m) - 1;
-            m &= m - 1;
-            if (sub == rr) {
-              float x[4];
-              load4_as_float<E>(Qb + (qbase + 64 * k + b) * (int64_t)(DIM * ES) + 4 * f * ES, x);
+      for (int u = 0; u < U; ++u) {
+        for (int rr = 0; rr < RPI; ++rr) {
 #pragma unroll
-              for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(g, x[t], v[t]);
+          for (int k = 0; k < NH; ++k) {
+            if (k >= nh) break;
+            uint64_t m = __ballot(key[k] == r0 + u * RPI + rr);
+            while (m != 0ull) {
+              const int b = __ffsll((unsigned long long)m) - 1;
+              m &= m - 1;
+              if (sub == rr) {
+                float x[4];
+                load4_as_float<E>(Qb + (qbase + 64 * k + b) * (int64_t)(DIM * ES) + 4 * f * ES, x);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[u][t] = __builtin_fmaf(g, x[t], v[u][t]);
+              }
             }
           }
         }
       }
     }
-    const int row = r0 + sub;
-    if (sub < RPI && row < r_end) {
-      const f32x4 w = {v[0], v[1], v[2], v[3]};
-      __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * RPI + sub;
+      if (sub < RPI && row < r_end) {
+        const f32x4 w = {v[u][0], v[u][1], v[u][2], v[u][3]};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f));
+      }
     }
   }
 }

@@ -53,7 +53,7 @@ enum GdMode : int {
 // pairwise / kd grad_D: at least this many waves per document, and enough
 // over the batch to fill the chip (few long documents split finer)
 constexpr int kGdPairsMinParts = 4;
-constexpr int64_t kGdPairsWaves = 16384;
+constexpr int64_t kGdPairsWaves = 65536;
 constexpr int64_t kGdPairsMinRows = 64;   // rows a wave streams, at least
 constexpr int kFzThreads = 512;        // threads of the fused grad_D workgroup
 constexpr int kFzMaxHitsPerWave = 2048; // hits one sorting wave of it ranks
