@@ -186,7 +186,12 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
   } else {
     p.n_cg = cdiv(Lq, p.SPW);
     int64_t pairs = p.n_docs * p.n_cg;
-    int64_t want = 4096;
+    // about 6 waves per SIMD: documents are split along Ld (the chunk maxima
+    // merge exactly) until that many waves stream; measured on kd (4096
+    // documents of 1030 rows, now 2 chunks each) and long rerank (64 of
+    // 32768 rows): 4096 waves left both below 0.7 of HBM peak, 16384 made
+    // the merge cost more than the split saved
+    int64_t want = 6144;
     int64_t nch = pairs >= want ? 1 : cdiv(want, pairs);
     int64_t max_nch = p.ntiles_max >= 4 ? p.ntiles_max / 4 : 1;
     if (nch > max_nch) nch = max_nch;
