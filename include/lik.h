@@ -45,7 +45,7 @@
  *   LIK_ERR_INVALID_ARG   null required pointer, negative or overflowing
  *                         size, unknown dtype, misaligned pointer, workspace
  *                         too small;
- *   LIK_ERR_UNSUPPORTED   a valid request this build does not implement
+ *   LIK_ERR_UNSUPPORTED   a valid request the library does not implement
  *                         (see lik_supported_dim; backward with Ld >
  *                         16000; all-pairs with Nd >= 2^23, Ld >
  *                         261120 or Nq * Lq > 2^30; no gfx950 device);
@@ -96,7 +96,7 @@ const char* lik_status_string(lik_status s);
 /* Detail of the last non-OK status returned on this host thread ("" if none). */
 const char* lik_last_error(void);
 
-/* 1 if the embedding dim `dim` has kernels in this build, else 0. */
+/* 1 if the embedding dim `dim` has kernels in the library, else 0. */
 int lik_supported_dim(int64_t dim);
 
 /*

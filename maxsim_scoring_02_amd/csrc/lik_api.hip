@@ -108,7 +108,7 @@ lik_status check_shapes(lik_dtype dtype, Shapes& s) {
 lik_status check_supported(lik_dtype dtype, const Shapes& s) {
   (void)dtype;
   if (s.dim == 0 || !lik::fwd_dim_supported(s.dim))
-    return fail(LIK_ERR_UNSUPPORTED, "embedding dim %lld has no kernel in this build (64, 128, 256)",
+    return fail(LIK_ERR_UNSUPPORTED, "embedding dim %lld has no kernel in this library (64, 128, 256)",
                 (long long)s.dim);
   if (s.layout == lik::kAllPairs && (s.nd_or_n > lik::kApMaxDocIndex || s.Ld > lik::kApMaxLd))
     return fail(LIK_ERR_UNSUPPORTED, "all-pairs supports Nd <= %lld and Ld <= %lld (got %lld, %lld)",
