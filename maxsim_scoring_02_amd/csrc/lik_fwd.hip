@@ -353,7 +353,10 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index is uniform: held in a scalar register, the load issue and
+  // its LDS addresses below need no per-lane branches or lane reads
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
 
   // Workgroups are dispatched round-robin over the 8 XCDs.  Every doc group
@@ -740,7 +743,8 @@ __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
   static_assert(G::kTileChunks % kWave == 0, "tile chunks must split over a wave");
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int h = lane >> 5, r = lane & 31;
   const int64_t unit = (int64_t)blockIdx.x * kPrWaves + wave;
   if (unit >= a.n_units) return;          // whole wave leaves; no workgroup barriers below
