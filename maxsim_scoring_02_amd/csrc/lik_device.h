@@ -165,64 +165,10 @@ struct Pad {
   static constexpr int kTileBytes = kTile * kStride;
 };
 
-// Mask the rows of a tile that are not valid (-inf never wins a max).  The
-// per-element row validity is computed once and applied to all NB blocks.
-template <int NB>
-__device__ __forceinline__ void tiles_mask(f32x16 (&acc)[NB], uint32_t word, int h) {
-  const uint32_t w = word >> (4 * h);
-  bool ok[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) ok[v] = (w >> (8 * (v >> 2) + (v & 3))) & 1u;
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[b][v] = ok[v] ? acc[b][v] : -__builtin_inff();
-}
-
-// Largest of a lane's 16 accumulator values (a tree of 3-input maxima).
-__device__ __forceinline__ float max16(const f32x16& acc) {
-  const float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
-  const float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
-  const float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
-  const float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
-  const float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
-  const float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
-  const float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
-  return __builtin_fmaxf(m1, m2);
-}
-
-// Fold two consecutive tiles (t, t+1) at once: one comparison with the
-// running max and at most one copy of 16 values, from the tile holding the
-// pair's maximum (the earlier tile on ties).
-__device__ __forceinline__ void state_fold_pair(BlockState& s, const f32x16& xa,
-                                                const f32x16& xb, int t) {
-  const float ta = max16(xa), tb = max16(xb);
-  const float tm = __builtin_fmaxf(ta, tb);
-  if (tm > s.run_max) {
-    s.run_max = tm;
-    const bool useb = tb > ta;
-    s.best_tile = useb ? t + 1 : t;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s.best_val[v] = useb ? xb[v] : xa[v];
-  }
-}
-
-// Fold a masked tile into the running state.  The copy of the tile's values
-// runs only in the lanes whose maximum improved (strict '>': the earlier tile
-// keeps ties), and is skipped by the whole wave when no lane improved.
-__device__ __forceinline__ void state_fold_sparse(BlockState& s, const f32x16& acc, int t) {
-  const float tmax = max16(acc);
-  if (tmax > s.run_max) {
-    s.run_max = tmax;
-    s.best_tile = t;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s.best_val[v] = acc[v];
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Lean fold for the all-pairs hot loop.  VALU time there adds to MFMA time
-// almost one for one, so the fold is written to issue as few VALU
+// Lean fold for the all-pairs hot loop.  The fold's VALU work mostly runs
+// while no MFMA is in flight on the SIMD (the waves sharing it tend to
+// multiply and fold in step), so it is written to issue as few VALU
 // instructions as possible:
 // - a 3-input max tree written directly (the generic fmax path re-quiets
 //   NaNs of unknown operands first; inputs are finite or -inf here);
@@ -287,33 +233,6 @@ __device__ __forceinline__ void state_begin(BlockState& s, int t0) {
   s.best_tile = t0;
 }
 
-// Fold tiles t and t+1 (strict '>' keeps the earlier tile, and within the
-// pair the earlier tile wins ties).
-__device__ __forceinline__ void state_fold_pair_lean(BlockState& s, const f32x16& xa,
-                                                     const f32x16& xb, int t) {
-  const float ta = max16_lean(xa), tb = max16_lean(xb);
-  const float tm = vmax2(ta, tb);
-  const bool better = tm > s.run_max;
-  const bool useb = tb > ta;
-  const uint64_t lanes = __builtin_amdgcn_ballot_w64(better);
-  const uint64_t ub = __builtin_amdgcn_ballot_w64(useb);
-  s.run_max = better ? tm : s.run_max;
-  s.best_tile = better ? t + (int)useb : s.best_tile;
-  sel_copy8<0>(s.best_val, xa, xb, lanes, ub);
-  sel_copy8<8>(s.best_val, xa, xb, lanes, ub);
-}
-
-// Fold one tile t.
-__device__ __forceinline__ void state_fold_one_lean(BlockState& s, const f32x16& x, int t) {
-  const float tm = max16_lean(x);
-  const bool better = tm > s.run_max;
-  const uint64_t lanes = __builtin_amdgcn_ballot_w64(better);
-  s.run_max = better ? tm : s.run_max;
-  s.best_tile = better ? t : s.best_tile;
-  sel_copy8<0>(s.best_val, x, x, lanes, 0);
-  sel_copy8<8>(s.best_val, x, x, lanes, 0);
-}
-
 // Fold one step of the hot loop: tiles t and t+1 when `two`, else tile t
 // alone (xb ignored); nothing when `step` is false.
 __device__ __forceinline__ void state_fold_step(BlockState& s, const f32x16& xa,
@@ -331,35 +250,8 @@ __device__ __forceinline__ void state_fold_step(BlockState& s, const f32x16& xa,
   sel_copy8<8>(s.best_val, xa, xb, lanes, ub);
 }
 
-// Leaner state: the running max and the absolute doc row that reached it
-// (lowest row on ties), resolved inside each tile as it is folded.
-struct RowState {
-  float run_max;
-  int best_row;
-};
-
-__device__ __forceinline__ void rowstate_init(RowState& s) {
-  s.run_max = -__builtin_inff();
-  s.best_row = 0;
-}
-
-__device__ __forceinline__ void rowstate_fold(RowState& s, const f32x16& acc, int t, int h) {
-  const float m01 = __builtin_fmaxf(__builtin_fmaxf(acc[0], acc[1]), acc[2]);
-  const float m02 = __builtin_fmaxf(__builtin_fmaxf(acc[3], acc[4]), acc[5]);
-  const float m03 = __builtin_fmaxf(__builtin_fmaxf(acc[6], acc[7]), acc[8]);
-  const float m04 = __builtin_fmaxf(__builtin_fmaxf(acc[9], acc[10]), acc[11]);
-  const float m05 = __builtin_fmaxf(__builtin_fmaxf(acc[12], acc[13]), acc[14]);
-  const float m1 = __builtin_fmaxf(__builtin_fmaxf(m01, m02), m03);
-  const float m2 = __builtin_fmaxf(__builtin_fmaxf(m04, m05), acc[15]);
-  const float tmax = __builtin_fmaxf(m1, m2);
-  int kk = 15;
-#pragma unroll
-  for (int v = 14; v >= 0; --v) kk = (acc[v] == tmax) ? v : kk;
-  const bool better = tmax > s.run_max;
-  s.run_max = better ? tmax : s.run_max;
-  s.best_row = better ? t * kTile + acc_row(kk, h) : s.best_row;
-}
-
+// Fold one tile of the pairwise/kd kernel: rows the validity word masks are
+// set to -inf first (a full word skips that).
 __device__ __forceinline__ void state_update(BlockState& s, f32x16 acc, uint32_t word, int t, int h) {
   if (word != 0xffffffffu) tile_mask(acc, word, h);
   state_fold(s, acc, t);
