@@ -106,3 +106,20 @@ def test_training_step_forward_loss_backward():
     rQ, rD = oracle.maxsim_allpairs_bwd(Qn, Dn, rg, merged, qmn, dmn)
     for x, y in ((gQ.cpu().numpy(), rQ), (gD.cpu().numpy(), rD)):
         assert np.all(np.abs(x - y) <= 1e-3 * np.abs(y) + 1e-5 * np.abs(y).max())
+
+
+def test_loss_without_gradient_output():
+    rng = np.random.default_rng(83)
+    S = torch.from_numpy((rng.standard_normal((70, 33)) * 5).astype(np.float32)).cuda()
+    lab = torch.from_numpy(rng.integers(0, 33, size=70).astype(np.int32)).cuda()
+    l1, r1, g1 = _lib.lik_ce_rows(S, lab, 2.5)
+    l2, r2, g2 = _lib.lik_ce_rows(S, lab, 2.5, want_grad=False)
+    assert g2 is None and g1 is not None
+    assert torch.equal(l1, l2) and torch.equal(r1, r2)
+
+
+def test_empty_documents_in_a_row():
+    # scores of empty documents are -1e9: a row of them has loss log C
+    S = torch.full((3, 5), -1e9, dtype=torch.float32, device="cuda")
+    S[1, 2] = 4.0
+    _check(S.cpu().numpy())
