@@ -11,9 +11,9 @@
 //
 //   grad_Q
 //     gradq_xcd_kernel     all-pairs with many documents: the documents are cut
-//                          into 8 slices, one per XCD, so each XCD gathers from an
-//                          L2-resident slice of D; gradq_reduce_kernel adds the
-//                          slice partials in slice order
+//                          into slices bound to XCDs (workgroup b runs on XCD
+//                          b % 8 and takes slice b % slices); gradq_reduce_kernel
+//                          adds the slice partials in slice order
 //     gradq_kernel         few documents per query (pairwise, kd, small Nd)
 //   grad_D
 //     gradd_fused_kernel   all-pairs: per document, a stable counting sort of
@@ -121,9 +121,10 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // grad_Q, all-pairs, XCD-sliced.  Workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup b runs on XCD b % 8; it gathers only from document
-// slice b % gq_slices, and with 8 slices each XCD reads one eighth of D,
-// which stays in that XCD's L2.  Thread = (query token, 16-byte chunk); all
-// its row loads of a round are independent.  Partials go to gq_part.
+// slice b % gq_slices, so each XCD reads 1 / gq_slices of D (with 2 slices,
+// even XCDs one half and odd XCDs the other; fewer slices write fewer
+// partials).  Thread = (query token, 16-byte chunk); all its row loads of a
+// round are independent.  Partials go to gq_part.
 // ---------------------------------------------------------------------------
 template <Elem E, int DIM>
 __global__ __launch_bounds__(256) void gradq_xcd_kernel(BwdArgs a) {

@@ -280,10 +280,19 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
     if (parts < kGdPairsMinParts) parts = kGdPairsMinParts;
     b.gd_parts = (int)parts;
   }
-  // (rows of one slice are indexed with 32 bits)
+  // grad_Q over many documents: the documents are cut into slices bound to
+  // XCDs, each gathered by its own workgroups, then added in slice order.
+  // When D takes at most half the last-level cache (128 of 256 MB), two slices (even and odd
+  // XCDs) write the fewest partials; a larger D is read from HBM, and one
+  // slice per XCD fetches each gathered row once.  Measured: in-batch text
+  // (D 19.7 MB) 81 / 79 / 78 / 102 us of backward with 8 / 4 / 2 / 1 slices;
+  // long documents (D 2.1 GB) 777 us with 8 slices, 825 with 2.  (Rows of one
+  // slice are indexed with 32 bits.)
+  const int64_t d_bytes = f.n_docs * Ld * dim * esize;
+  const int slices = d_bytes <= (int64_t(128) << 20) ? 2 : 8;
   if (layout == kAllPairs && f.n_docs >= kGqSliceMinDocs && Lq > 0 && Ld > 0 &&
-      cdiv(f.n_docs, 8) * Ld < (int64_t(1) << 31))
-    b.gq_slices = 8;
+      cdiv(f.n_docs, slices) * Ld < (int64_t(1) << 31))
+    b.gq_slices = slices;
 
   size_t off = 0;
   if (b.recompute && Lq > 0) {
