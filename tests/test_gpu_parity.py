@@ -432,3 +432,51 @@ def test_euler_identity_on_gpu_outputs():
     ld = float(np.sum(Dn.astype(np.float64) * gD))
     assert abs(lq - rhs) <= 1e-4 * max(1.0, abs(rhs))
     assert abs(ld - rhs) <= 1e-4 * max(1.0, abs(rhs))
+
+
+# ------------------------------------------------------------- op memory
+
+def test_op_memory_is_linear_in_batch():
+    """Peak device memory of forward + backward on in-batch text shapes at
+    B = 32..256: exactly what the operator's outputs, argmax, gradients and
+    workspaces take (the library allocates nothing itself), with no term of
+    the [B, B, Lq, Ld] similarity grid the naive path holds."""
+    from maxsim_scoring_02_amd import _lib
+
+    rows = []
+    for B in (32, 64, 128, 256):
+        w = wl.inbatch_text(B=B, Nd=B)
+        Q, D = w.Q.cuda(), w.D.cuda()
+        dm = w.d_mask.cuda()
+        g = w.grad.cuda()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        s, a = _lib.lik_maxsim_fwd(Q, D, None, dm)
+        gQ, gD = _lib.lik_maxsim_bwd(Q, D, g, a, None, dm)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        Lq, Ld, dim = 32, 300, 128
+        L = _lib.lib()
+        wsf = L.lik_workspace_bytes(_lib.LIK_OP_FWD, B, Lq, B, Ld, dim, _lib.LIK_BF16, 1 | 2)
+        wsb = L.lik_workspace_bytes(_lib.LIK_OP_BWD, B, Lq, B, Ld, dim, _lib.LIK_BF16, 1 | 2)
+        outs = B * B * 4 + B * B * Lq * 4 + B * Lq * dim * 4 + B * Ld * dim * 4
+        rnd = lambda n: (n + 511) // 512 * 512            # the allocator's block size
+        # outputs and workspaces, plus 1 MiB for the binding's small
+        # argument copies (mask bytes, upstream grad)
+        bound = rnd(B * B * 4) + rnd(B * B * Lq * 4) + rnd(B * Lq * dim * 4) + \
+            rnd(B * Ld * dim * 4) + rnd(max(wsf, 256)) + rnd(max(wsb, 256)) + (1 << 20)
+        grid = B * B * Lq * Ld * 4
+        rows.append((B, peak, outs, grid))
+        say(f"[memory] B={B}: peak {peak / 2**20:.1f} MiB, outputs {outs / 2**20:.1f} MiB, "
+            f"workspaces {(wsf + wsb) / 2**20:.1f} MiB, naive grid {grid / 2**30:.2f} GiB")
+        assert outs <= peak <= bound
+        assert peak < grid / 4
+        del s, a, gQ, gD
+    for B, p, o, _ in rows:
+        # beyond the outputs, memory is linear in B: per query at most two
+        # grad_Q partial rows (Lq x dim x 4 bytes each) and the tile words
+        assert p - o <= B * (2 * 32 * 128 * 4 + 2 * 4 * 10 + 64) + (1 << 20)
+    for (B1, p1, o1, g1), (B2, p2, o2, g2) in zip(rows, rows[1:]):
+        # the naive grid outgrows the operator's memory as B doubles
+        assert g2 / p2 > 1.5 * (g1 / p1)
