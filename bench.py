@@ -28,8 +28,10 @@ gradients written.
 Other workloads (--workload): inbatch-pages, kd-candidates, long-docs,
 long-rerank, or `all` (one line each); `next` runs the long-context backward
 (long-docs-bwd, long-rerank-bwd: the long-document inputs with a Gaussian
-upstream grad, forward + backward) and kd-loss-head (the kd-candidates
-inputs with the negative-doc cross-entropy as the loss head).
+upstream grad, forward + backward), kd-loss-head (the kd-candidates
+inputs with the negative-doc cross-entropy as the loss head) and
+inbatch-text-f32 (the in-batch text step with float32 inputs, computed
+exactly on the fp32 MFMA and reported against its 157.3 TFLOP/s peak).
 
 In-batch pages and kd-loss-head steps run the loss head on the GPU between
 forward and backward (cross-entropy over the score rows, library entry
@@ -57,6 +59,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MaxSim fwd+bwd TFLOP/s (% MFMA peak); pairwise rerank GB/s (% HBM peak)"
 PEAK_MFMA_16BIT = 2500.0        # TFLOP/s, MI355X dense bf16/fp16
+PEAK_MFMA_F32 = 157.3           # TFLOP/s, MI355X dense fp32 (matrix)
 PEAK_HBM = 8000.0               # GB/s, MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -266,6 +269,11 @@ def make_workload(name: str):
         # diagonal of the step's own scores, on the GPU inside every step
         w.meta["loss_head"] = "diag"
         return w, True
+    if name == "inbatch-text-f32":
+        # float32 inputs, computed exactly on the fp32 MFMA (no downcast)
+        w = wl.inbatch_text(dtype="f32")
+        w.name = name
+        return w, True
     if name == "kd-loss-head":
         # the pages' loss-head benchmark shape (B 256 x 16 candidates, Lq 32,
         # Ld 1030): kd forward, negative-doc cross-entropy with candidate 0
@@ -305,6 +313,7 @@ DOMINANT = {  # kernel whose roofline is reported, and its bound
     "long-docs-bwd": ("allpairs_fwd", "mfma"),
     "long-rerank-bwd": ("pairs_fwd", "hbm"),
     "kd-loss-head": ("pairs_fwd", "hbm"),
+    "inbatch-text-f32": ("allpairs_fwd", "mfma"),
 }
 
 
@@ -470,7 +479,7 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
         value = flops / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
         achieved = f_fwd / (t_kern * 1e-3) / 1e12
-        peak = PEAK_MFMA_16BIT
+        peak = PEAK_MFMA_F32 if w.dtype == "f32" else PEAK_MFMA_16BIT
         rl_unit = "TFLOP/s"
     else:
         nbytes = b_fwd + (b_bwd if backward else 0.0)
@@ -576,7 +585,7 @@ def main():
         copy_calibration(args.copy_calibration, max(args.steps, 1))
         return
     groups = {"all": ["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"],
-              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head"]}
+              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head", "inbatch-text-f32"]}
     names = groups.get(args.workload, [args.workload])
     for i, name in enumerate(names):
         line = bench_one(name, args.steps, args.warmup,
