@@ -113,6 +113,19 @@ def _embeddings(Q: torch.Tensor, D: torch.Tensor) -> int:
     return DTYPE_CODE[Q.dtype]
 
 
+def _same_batch(Q: torch.Tensor, D: torch.Tensor, layout: str) -> None:
+    """Pairwise and kd pair query b with document (row) b of D.  The C ABI
+    receives B only, so a D with fewer rows would be read past its end on the
+    device: the shapes are checked here, before anything is launched."""
+    want = 3 if layout == "pairwise" else 4
+    if Q.dim() != 3 or D.dim() != want:
+        raise ValueError(f"{layout}: Q must be [B, Lq, dim] and D "
+                         f"{'[B, Ld, dim]' if want == 3 else '[B, N, Ld, dim]'}")
+    if D.shape[0] != Q.shape[0]:
+        raise ValueError(f"{layout} Q and D must share the batch size "
+                         f"(Q has {Q.shape[0]}, D has {D.shape[0]})")
+
+
 def _flags(argmax_given: bool, dm, qm) -> int:
     """lik_workspace_bytes flags: bit 0 argmax, bit 1 document mask, bit 2 query mask."""
     return (1 if argmax_given else 0) | (2 if dm is not None else 0) | (4 if qm is not None else 0)
@@ -159,11 +172,10 @@ def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
 
 def lik_maxsim_pairwise_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     """Pairwise: Q [B, Lq, dim] x D [B, Ld, dim] -> scores [B], argmax [B, Lq]."""
+    _same_batch(Q, D, "pairwise")
     dt = _embeddings(Q, D)
     B, Lq, dim = Q.shape
-    B2, Ld, _ = D.shape
-    if B2 != B:
-        raise ValueError("pairwise Q and D must share the batch size")
+    _, Ld, _ = D.shape
     qm = _mask(q_mask, (B, Lq), Q.device)
     dm = _mask(d_mask, (B, Ld), Q.device)
     scores = torch.empty((B,), dtype=torch.float32, device=Q.device)
@@ -179,11 +191,10 @@ def lik_maxsim_pairwise_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
 
 def lik_maxsim_kd_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     """kd: Q [B, Lq, dim] x D [B, N, Ld, dim] -> scores [B, N], argmax [B, N, Lq]."""
+    _same_batch(Q, D, "kd")
     dt = _embeddings(Q, D)
     B, Lq, dim = Q.shape
-    B2, N, Ld, _ = D.shape
-    if B2 != B:
-        raise ValueError("kd Q and D must share the batch size")
+    _, N, Ld, _ = D.shape
     qm = _mask(q_mask, (B, Lq), Q.device)
     dm = _mask(d_mask, (B, N, Ld), Q.device)
     scores = torch.empty((B, N), dtype=torch.float32, device=Q.device)
@@ -235,6 +246,7 @@ def lik_maxsim_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
 
 def lik_maxsim_pairwise_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
                             need_grad_q=True, need_grad_d=True) -> Tuple:
+    _same_batch(Q, D, "pairwise")
     dt = _embeddings(Q, D)
     B, Lq, dim = Q.shape
     _, Ld, _ = D.shape
@@ -255,6 +267,7 @@ def lik_maxsim_pairwise_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=
 
 def lik_maxsim_kd_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
                       need_grad_q=True, need_grad_d=True) -> Tuple:
+    _same_batch(Q, D, "kd")
     dt = _embeddings(Q, D)
     B, Lq, dim = Q.shape
     _, N, Ld, _ = D.shape

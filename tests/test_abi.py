@@ -205,3 +205,25 @@ def test_loss_head_rejects_invalid_arguments(L, kw, msg):
 
 def test_loss_head_zero_rows_is_a_noop(L):
     assert L.lik_ce_rows(None, 0, 7, None, 1.0, None, None, None, None) == 0
+
+
+@pytest.mark.parametrize("layout", ["pairwise", "kd"])
+def test_binding_rejects_batch_mismatch_before_any_launch(layout, monkeypatch):
+    """The C ABI gets B only, so a D with another batch size would be read
+    past its end (or partly ignored) on the device: the binding refuses it
+    before the library is even loaded, in the forward and the backward."""
+    import torch
+
+    def no_library():
+        raise AssertionError("the library was reached")
+
+    monkeypatch.setattr(_lib, "lib", no_library)
+    Q = torch.zeros((4, 8, 64), dtype=torch.bfloat16)
+    D = (torch.zeros((3, 40, 64), dtype=torch.bfloat16) if layout == "pairwise"
+         else torch.zeros((3, 2, 40, 64), dtype=torch.bfloat16))
+    g = torch.zeros((4,) if layout == "pairwise" else (4, 2), dtype=torch.float32)
+    for call in (lambda: _lib.FORWARD[layout](Q, D),
+                 lambda: _lib.BACKWARD[layout](Q, D, g),
+                 lambda: _lib.BACKWARD[layout](Q, D[:, None] if layout == "pairwise" else D[0], g)):
+        with pytest.raises(ValueError, match="batch size|must be"):
+            call()

@@ -420,6 +420,79 @@ def test_admissible_argmax_accepts_only_ties():
         oracle.admissible_argmax(r2, np.array([[[1]]]), Q, D2, None, "allpairs")
 
 
+def _admit_cases(layout):
+    """One query token whose two best document tokens tie exactly (rows 1
+    and 3 equal the query token, row 0 is masked and would beat them, row 2
+    is 0.5 below), in the given layout."""
+    q = np.array([1.0, 0.0, 0.0])
+    rows = np.array([[2.0, 0.0, 0.0], [1.0, 0.0, 0.0], [0.5, 0.0, 0.0], [1.0, 0.0, 0.0]])
+    dmask_row = np.array([False, True, True, True])
+    other = np.array([[0.1] * 3, [0.3] * 3, [0.2] * 3, [0.9] * 3])   # a clear max at row 3
+    if layout == "allpairs":
+        Q = q[None, None]
+        D = np.stack([other, rows])                    # the tie sits in document 1
+        dm = np.stack([np.ones(4, bool), dmask_row])
+        r = oracle.maxsim_allpairs(Q, D, None, dm)
+        pos = (0, 1, 0)
+    elif layout == "pairwise":
+        Q = np.stack([np.array([[0.0, 0.0, 1.0]]), q[None]])   # batch 2, tie in pair 1
+        D = np.stack([other, rows])
+        dm = np.stack([np.ones(4, bool), dmask_row])
+        r = oracle.maxsim_pairwise(Q, D, None, dm)
+        pos = (1, 0)
+    else:
+        Q = np.stack([np.array([[0.0, 0.0, 1.0]]), q[None]])
+        D = np.stack([np.stack([other, other]), np.stack([other, rows])])   # [2, 2, 4, 3]
+        dm = np.ones((2, 2, 4), bool)
+        dm[1, 1] = dmask_row
+        r = oracle.maxsim_kd(Q, D, None, dm)
+        pos = (1, 1, 0)
+    return Q, D, dm, r, pos
+
+
+@pytest.mark.parametrize("layout", ["allpairs", "pairwise", "kd"])
+def test_admissible_argmax_each_layout(layout):
+    """The tie admission of every layout: the oracle keeps the lowest of two
+    exactly tied rows; another implementation's pick of the other tied row
+    is adopted, while a clearly worse row, a masked row (even one whose
+    similarity is larger), an index past the document and a difference at a
+    non-tie position are all refused."""
+    Q, D, dm, r, pos = _admit_cases(layout)
+    assert r.argmax[pos] == 1 and r.tie[pos]
+    assert not r.tie[tuple(0 for _ in pos)]            # the other entry is no tie
+
+    def with_index(j, at=pos):
+        o = r.argmax.copy()
+        o[at] = j
+        return o
+
+    merged = oracle.admissible_argmax(r, with_index(3), Q, D, dm, layout)
+    assert merged[pos] == 3
+    assert np.array_equal(np.delete(merged.ravel(), np.ravel_multi_index(pos, merged.shape)),
+                          np.delete(r.argmax.ravel(), np.ravel_multi_index(pos, merged.shape)))
+    for bad in (2, 0, 4, -1):                           # worse, masked, out of range, sentinel
+        with pytest.raises(AssertionError):
+            oracle.admissible_argmax(r, with_index(bad), Q, D, dm, layout)
+    zero = tuple(0 for _ in pos)
+    with pytest.raises(AssertionError):                 # no tie there: must match exactly
+        oracle.admissible_argmax(r, with_index(r.argmax[zero] + 1, zero), Q, D, dm, layout)
+    # an index only as good as the tie within 1e-5 is admitted, a slightly
+    # worse one (by more than 1e-5) is not
+    D2 = np.array(D, dtype=np.float64, copy=True)
+    row3 = (1, 3) if layout != "kd" else (1, 1, 3)
+    D2[row3][0] = 1.0 - 5e-6
+    r2 = {"allpairs": oracle.maxsim_allpairs, "pairwise": oracle.maxsim_pairwise,
+          "kd": oracle.maxsim_kd}[layout](Q, D2, None, dm)
+    assert r2.tie[pos]
+    assert oracle.admissible_argmax(r2, with_index(3), Q, D2, dm, layout)[pos] == 3
+    D2[row3][0] = 1.0 - 5e-5
+    r3 = {"allpairs": oracle.maxsim_allpairs, "pairwise": oracle.maxsim_pairwise,
+          "kd": oracle.maxsim_kd}[layout](Q, D2, None, dm)
+    assert not r3.tie[pos]
+    with pytest.raises(AssertionError):
+        oracle.admissible_argmax(r3, with_index(3), Q, D2, dm, layout)
+
+
 def test_block_helper_matches_layouts():
     Q, D, qm, dm, g = _tiny_case(19)
     r = oracle.maxsim_allpairs(Q, D, qm, dm)
