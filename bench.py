@@ -39,6 +39,14 @@ lik_ce_rows); its time is part of the step and of `config.bwd_ms`.
 
 `cpu_baseline` is the CPU oracle timed on this machine's cores on a bounded
 sample of the same workload (the sample is named in the JSON).
+
+`roofline.frac` is the dominant kernel alone against its peak;
+`roofline.step_frac` is the whole step (`value`) against the same peak.  The
+default line also carries `secondary`: the metric's memory-bound half, the
+long-document pairwise rerank (64 query-document pairs, 32 query tokens
+against 32768 document tokens,
+fp16, forward only) in GB/s and as a fraction of HBM peak, timed in the same
+run with the same step counts (`--no-secondary` leaves it out).
 """
 
 from __future__ import annotations
@@ -304,6 +312,9 @@ def make_workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
+# workloads whose line also carries the metric's memory-bound half
+SECONDARY = {"inbatch-text": "long-rerank"}
+
 DOMINANT = {  # kernel whose roofline is reported, and its bound
     "inbatch-text": ("allpairs_fwd", "mfma"),
     "inbatch-pages": ("allpairs_fwd", "mfma"),
@@ -526,6 +537,9 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
             "traffic": traffic,
             "kernel_ms": round(t_kern, 5),
             "timed_as": "main forward kernel alone, HIP events recorded by the library on its stream",
+            # the whole step (every kernel of forward and backward) against
+            # the same peak: `value` / `peak`
+            "step_frac": round(value / peak, 4),
         },
         "cpu_baseline": None,
     }
@@ -568,6 +582,8 @@ def main():
                     help="untimed steps first (the GPU clock needs tens of ms of load to settle)")
     ap.add_argument("--workload", default="inbatch-text")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="do not time the long-document rerank alongside the in-batch step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of a workload, run plain device copies of MIB MiB "
                          "(reference kernel for scaling HBM counters)")
@@ -590,6 +606,25 @@ def main():
     for i, name in enumerate(names):
         line = bench_one(name, args.steps, args.warmup,
                          with_cpu=(not args.no_cpu_baseline))
+        if name in SECONDARY and not args.no_secondary:
+            # the metric's second half, timed in the same run: the
+            # memory-bound long-document rerank (pairwise, forward only)
+            torch.cuda.empty_cache()
+            sec = bench_one(SECONDARY[name], args.steps, args.warmup, with_cpu=False)
+            line["secondary"] = {
+                "metric": "pairwise rerank GB/s (% HBM peak)",
+                "workload": sec["config"]["workload"],
+                "value": sec["value"],
+                "unit": sec["unit"],
+                "frac": sec["roofline"]["step_frac"],
+                "ms_per_step": sec["ms_per_step"],
+                "dtype": sec["dtype"],
+                "Q": sec["config"]["Q"],
+                "D": sec["config"]["D"],
+                "kernel": sec["roofline"]["kernel"],
+                "kernel_ms": sec["roofline"]["kernel_ms"],
+                "kernel_frac": sec["roofline"]["frac"],
+            }
         print(json.dumps(line), flush=True)
         if i + 1 < len(names):
             torch.cuda.empty_cache()

@@ -133,6 +133,30 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq,
                            lik_dtype dtype, int flags);
 
 /*
+ * Launch-plan introspection (not needed for scoring): one value of the plan
+ * the library would use for a call with these shapes and flags (same
+ * arguments as lik_workspace_bytes), so that tests can show they exercise
+ * the same kernels and work split as a given workload.  `key` is a NUL-
+ * terminated name:
+ *   forward  "nb" (32-column MFMA blocks per wave), "upw" (document units per
+ *            all-pairs workgroup), "n_groups", "n_sb" (query slot blocks),
+ *            "nchunks" (pieces a document is split into), "tpc" (32-row
+ *            tiles per piece), "compact" (query tokens compacted), "partial"
+ *            (per-piece partials merged by a second kernel), "qpw" (whole
+ *            queries per wave, 0 = flattened), "n_units" (pairwise/kd waves);
+ *   backward every forward key (the plan of the recomputing forward) and
+ *            "gd_mode" (grad_D kernel: 0 workspace sort, 1 fused all-pairs,
+ *            2 pairwise/kd streaming), "gd_parts", "fz_split", "fz_sw",
+ *            "gq_slices", "recompute";
+ *   both     "workspace" (the same as lik_workspace_bytes).
+ * Returns -1 for an unknown key, a key of the other direction, or sizes
+ * lik_workspace_bytes rejects.  Host only; no device is touched.
+ */
+int64_t lik_plan_value(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or_n,
+                       int64_t ld, int64_t dim, lik_dtype dtype, int flags,
+                       const char* key);
+
+/*
  * All-pairs forward (README "Scoring interface", layer MaxSim):
  *   Q [Nq, Lq, dim] x D [Nd, Ld, dim] -> scores [Nq, Nd] float32.
  * q_mask [Nq, Lq] bytes or NULL; d_mask [Nd, Ld] bytes or NULL.

@@ -47,6 +47,7 @@ SIGNATURES = {
     "lik_supported_dim": ([_I64], _I),
     "lik_set_profile_events": ([_P, _P], _I),
     "lik_workspace_bytes": ([_I, _I64, _I64, _I64, _I64, _I64, _I, _I], _SZ),
+    "lik_plan_value": ([_I, _I64, _I64, _I64, _I64, _I64, _I, _I, ctypes.c_char_p], _I64),
     "lik_maxsim_fwd": (_FWD_ALLPAIRS, _I),
     "lik_maxsim_bwd": (_BWD_ALLPAIRS, _I),
     "lik_maxsim_pairwise_fwd": (_FWD_PAIRWISE, _I),
@@ -67,7 +68,7 @@ def header_functions() -> list:
     """Names of the functions declared in include/lik.h."""
     with open(HEADER_PATH) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^[a-z_ ]+?\**\s*\b(lik_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^[a-z0-9_ ]+?\**\s*\b(lik_[a-z_]+)\s*\(", text, re.M)))
 
 
 def lib() -> ctypes.CDLL:
@@ -150,6 +151,12 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 # ---------------------------------------------------------------------------
 # forward
 # ---------------------------------------------------------------------------
+
+def lik_plan_value(op: int, dims, dtype: int, flags: int, key: str) -> int:
+    """One value of the launch plan for a call (see include/lik.h); dims =
+    (nq_or_b, lq, nd_or_n, ld, dim) as for lik_workspace_bytes."""
+    return int(lib().lik_plan_value(op, *dims, dtype, flags, key.encode()))
+
 
 def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     """All-pairs: Q [Nq, Lq, dim] x D [Nd, Ld, dim] -> scores [Nq, Nd] float32,

@@ -259,6 +259,45 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or
       .total;
 }
 
+namespace {
+int64_t fwd_plan_value(const lik::FwdPlan& p, const char* key) {
+  struct KV { const char* k; int64_t v; };
+  const KV kv[] = {{"nb", p.NB},           {"upw", p.upw},         {"n_groups", p.n_groups},
+                   {"n_sb", p.n_sb},       {"nchunks", p.nchunks}, {"tpc", p.tpc},
+                   {"compact", p.compact}, {"partial", p.partial}, {"qpw", p.qpw},
+                   {"n_units", p.n_units}, {"n_cg", p.n_cg}};
+  for (const KV& e : kv)
+    if (std::strcmp(key, e.k) == 0) return e.v;
+  return -1;
+}
+}  // namespace
+
+int64_t lik_plan_value(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or_n, int64_t ld,
+                       int64_t dim, lik_dtype dtype, int flags, const char* key) {
+  if (!key) return -1;
+  const size_t ws = lik_workspace_bytes(op, nq_or_b, lq, nd_or_n, ld, dim, dtype, flags);
+  if (ws == SIZE_MAX) return -1;
+  if (std::strcmp(key, "workspace") == 0) return (int64_t)ws;
+  const int layout = (op == LIK_OP_FWD || op == LIK_OP_BWD)                   ? lik::kAllPairs
+                     : (op == LIK_OP_PAIRWISE_FWD || op == LIK_OP_PAIRWISE_BWD) ? lik::kPairwise
+                                                                                : lik::kKd;
+  const bool bwd = op == LIK_OP_BWD || op == LIK_OP_PAIRWISE_BWD || op == LIK_OP_KD_BWD;
+  const bool has_dmask = (flags & 2) != 0, arg = (flags & 1) != 0, has_qmask = (flags & 4) != 0;
+  if (!bwd)
+    return fwd_plan_value(lik::make_fwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim,
+                                             has_dmask, arg, has_qmask),
+                          key);
+  const lik::BwdPlan b = lik::make_bwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim,
+                                            has_dmask, arg, has_qmask);
+  struct KV { const char* k; int64_t v; };
+  const KV kv[] = {{"gd_mode", b.gd_mode},     {"gd_parts", b.gd_parts}, {"fz_split", b.fz_split},
+                   {"fz_sw", b.fz_sw},         {"gq_slices", b.gq_slices},
+                   {"recompute", b.recompute}};
+  for (const KV& e : kv)
+    if (std::strcmp(key, e.k) == 0) return e.v;
+  return fwd_plan_value(b.fwd, key);
+}
+
 lik_status lik_maxsim_fwd(const void* Q, const void* D, lik_dtype dtype, int64_t Nq, int64_t Lq,
                           int64_t Nd, int64_t Ld, int64_t dim, const uint8_t* q_mask,
                           const uint8_t* d_mask, float* scores, int32_t* argmax, void* workspace,

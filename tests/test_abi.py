@@ -26,7 +26,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = _lib.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), f"liblik.so does not export {n}"
     assert set(names) == set(_lib.SIGNATURES)
@@ -227,3 +227,19 @@ def test_binding_rejects_batch_mismatch_before_any_launch(layout, monkeypatch):
                  lambda: _lib.BACKWARD[layout](Q, D[:, None] if layout == "pairwise" else D[0], g)):
         with pytest.raises(ValueError, match="batch size|must be"):
             call()
+
+
+def test_plan_value_introspection(L):
+    """lik_plan_value reports the plans the entry points use: the workspace
+    size agrees with lik_workspace_bytes, keys of the other direction and
+    unknown keys give -1, and the in-batch text shape runs several document
+    units per all-pairs workgroup."""
+    dims = (256, 32, 256, 300, 128)
+    pv = lambda op, key, flags=3: _lib.lik_plan_value(op, dims, LIK_BF16, flags, key)
+    assert pv(LIK_OP_FWD, "workspace") == L.lik_workspace_bytes(LIK_OP_FWD, *dims, LIK_BF16, 3)
+    assert pv(LIK_OP_BWD, "workspace") == L.lik_workspace_bytes(LIK_OP_BWD, *dims, LIK_BF16, 3)
+    assert pv(LIK_OP_FWD, "upw") > 1 and pv(LIK_OP_FWD, "nb") == 2
+    assert pv(LIK_OP_FWD, "gq_slices") == -1 and pv(LIK_OP_FWD, "no such key") == -1
+    assert pv(LIK_OP_BWD, "upw") == pv(LIK_OP_FWD, "upw")
+    assert pv(LIK_OP_BWD, "recompute") == 0 and pv(LIK_OP_BWD, "recompute", 2) == 1
+    assert _lib.lik_plan_value(LIK_OP_FWD, (-1, 32, 4, 40, 128), LIK_BF16, 0, "upw") == -1
