@@ -145,9 +145,10 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq,
  *            (per-piece partials merged by a second kernel), "qpw" (whole
  *            queries per wave, 0 = flattened), "n_units" (pairwise/kd waves);
  *   backward every forward key (the plan of the recomputing forward) and
- *            "gd_mode" (grad_D kernel: 0 workspace sort, 1 fused all-pairs,
- *            2 pairwise/kd streaming), "gd_parts", "fz_split", "fz_sw",
- *            "gq_slices", "recompute";
+ *            "gd_mode" (grad_D kernel: 0 workspace sort, 1 sorted in LDS
+ *            per all-pairs document, 2 pairwise/kd streaming), "gd_parts",
+ *            "gs_split", "gs_sw", "gs_lds", "gq_ap" (all-pairs grad_Q by
+ *            document rounds), "gq_slices", "recompute";
  *   both     "workspace" (the same as lik_workspace_bytes).
  * Returns -1 for an unknown key, a key of the other direction, or sizes
  * lik_workspace_bytes rejects.  Host only; no device is touched.

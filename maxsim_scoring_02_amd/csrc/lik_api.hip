@@ -290,9 +290,9 @@ int64_t lik_plan_value(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or_n, 
   const lik::BwdPlan b = lik::make_bwd_plan(layout, (int)dtype, nq_or_b, lq, nd_or_n, ld, dim,
                                             has_dmask, arg, has_qmask);
   struct KV { const char* k; int64_t v; };
-  const KV kv[] = {{"gd_mode", b.gd_mode},     {"gd_parts", b.gd_parts}, {"fz_split", b.fz_split},
-                   {"fz_sw", b.fz_sw},         {"gq_slices", b.gq_slices},
-                   {"recompute", b.recompute}};
+  const KV kv[] = {{"gd_mode", b.gd_mode},     {"gd_parts", b.gd_parts}, {"gs_split", b.gs_split},
+                   {"gs_sw", b.gs_sw},         {"gq_ap", b.gq_ap},       {"gq_slices", b.gq_slices},
+                   {"recompute", b.recompute}, {"gs_lds", (int64_t)b.gs_lds}};
   for (const KV& e : kv)
     if (std::strcmp(key, e.k) == 0) return e.v;
   return fwd_plan_value(b.fwd, key);

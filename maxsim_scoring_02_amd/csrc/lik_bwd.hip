@@ -10,21 +10,27 @@
 // owner that adds its terms in an order fixed by the inputs alone.
 //
 //   grad_Q
-//     gradq_xcd_kernel     all-pairs with many documents: the documents are cut
-//                          into slices bound to XCDs (workgroup b runs on XCD
-//                          b % 8 and takes slice b % slices); gradq_reduce_kernel
-//                          adds the slice partials in slice order
+//     gradq_ap_kernel      all-pairs with many documents: a token's lanes take
+//                          16 documents per round, each lane preparing one
+//                          (row offset, weight) that the others read by a lane
+//                          broadcast; with several document slices (workgroup
+//                          b runs on XCD b % 8 and takes slice b % slices)
+//                          gradq_reduce_kernel adds the partials in slice order
 //     gradq_kernel         few documents per query (pairwise, kd, small Nd)
 //   grad_D
-//     gradd_fused_kernel   all-pairs: per document, a stable counting sort of
-//                          its hits by row in LDS, then lane groups sum equal
-//                          shares of the sorted hits; rows cut by a share
-//                          boundary are finished by the group where they start
+//     gradd_sorted_kernel  all-pairs: per document, one workgroup sorts its
+//                          hits by row (stable counting sort in LDS), then
+//                          lane groups sum equal shares of the sorted hits,
+//                          16 hits per round prepared one per lane; rows cut by
+//                          a share boundary are finished by the group where
+//                          they start
 //     gradd_pairs_kernel   pairwise / kd: four waves per document stream its
 //                          (mostly zero) rows and sum the few hit rows inline
 //     gradd_sort_*_kernel + gradd_rows_group_kernel
 //                          general fallback through the workspace
 #include <hip/hip_runtime.h>
+
+#include <utility>
 
 #include "lik_device.h"
 #include "lik_kernels.h"
@@ -49,9 +55,12 @@ struct BwdArgs {
   int layout;
   int key_bits;
   int gq_slices;
-  int fz_sw, fz_split;                      // fused grad_D: sorting waves, workgroups per doc
+  int gq_ap;                                // grad_Q by gradq_ap_kernel (else gradq_kernel)
+  int gs_sw, gs_split;                      // sorted grad_D: sorting waves, workgroups per doc
   int gd_parts;                             // pairwise / kd grad_D: waves per document
-  int fz_off_start, fz_off_cnt, fz_off_sorted, fz_off_gl, fz_off_union, fz_off_masks;  // LDS layout
+  int gs_masks;                             // sorted grad_D: ranks from LDS match masks
+  int gs_off_sorted, gs_off_start, gs_off_gl, gs_off_keys, gs_off_hist, gs_off_masks,
+      gs_off_part;                          // LDS layout
   uint64_t lq_magic;                        // ceil(2^32 / Lq): h / Lq for h < 2^16
   int64_t Nq, Lq, n_docs, Ld, K, H;
 };
@@ -119,20 +128,61 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// grad_Q, all-pairs, XCD-sliced.  Workgroups are dispatched round-robin over
-// the 8 XCDs, so workgroup b runs on XCD b % 8; it gathers only from document
-// slice b % gq_slices, so each XCD reads 1 / gq_slices of D (with 2 slices,
-// even XCDs one half and odd XCDs the other; fewer slices write fewer
-// partials).  Thread = (query token, 16-byte chunk); all its row loads of a
-// round are independent.  Partials go to gq_part.
+// Lane broadcasts inside a lane group of CPR lanes (one row chunk each): with
+// 16-lane groups a DPP row_newbcast (a VALU move, folded by the compiler into
+// the instruction that consumes it), otherwise a lane swap.
+// ---------------------------------------------------------------------------
+template <int CPR, int U>
+__device__ __forceinline__ int grp_bcast(int v, int base_lane) {
+  if constexpr (CPR == 16) {
+    (void)base_lane;
+    return __builtin_amdgcn_update_dpp(0, v, 0x150 + U, 0xf, 0xf, false);
+  } else {
+    return __shfl(v, base_lane + U);
+  }
+}
+template <int CPR, int U>
+__device__ __forceinline__ float grp_bcast_f(float v, int base_lane) {
+  return __int_as_float(grp_bcast<CPR, U>(__float_as_int(v), base_lane));
+}
+
+template <int... U, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, U...>, F&& f) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+// f(integral_constant<0>) ... f(integral_constant<N-1>), fully unrolled
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+__device__ __forceinline__ u32x4 ld_buf_16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+
+// Buffer descriptor over `bytes` bytes at `p` (bytes < 2^32): loads outside
+// it return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// grad_Q, all-pairs.  Thread = (query token, 16-byte chunk c of the row).
+// Documents are taken R at a time: lane c of a token looks up document k0 + c
+// (its argmax row, turned into a byte offset inside the document slice, and
+// its weight g[q, d]; row 0 and weight 0 when the document gives this token
+// nothing), then the token's lanes issue the R row gathers with those values
+// broadcast from lane u, and add g * row in document order.  With several
+// slices, workgroup b runs on XCD b % 8 and gathers only from slice
+// b % slices, so each XCD's L2 serves a fraction of D; partials go to gq_part.
 // ---------------------------------------------------------------------------
 template <Elem E, int DIM>
-__global__ __launch_bounds__(256) void gradq_xcd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void gradq_ap_kernel(BwdArgs a) {
   using G = Geo<E, DIM>;
   constexpr int EPC = ElemInfo<E>::kPerChunk;
   constexpr int CPR = G::kCPR;
   constexpr int TPB = 256 / CPR;           // query tokens per workgroup
-  constexpr int U = CPR < 16 ? CPR : 16;   // documents per round (one index load per lane)
+  constexpr int R = CPR < 16 ? CPR : 16;   // documents per round (one per lane)
   const int ns = a.gq_slices;
   const int sl = (int)(blockIdx.x % ns);
   const int64_t tb = blockIdx.x / ns;
@@ -145,45 +195,45 @@ __global__ __launch_bounds__(256) void gradq_xcd_kernel(BwdArgs a) {
   const int64_t q = qi / a.Lq, i = qi - q * a.Lq;
   const int64_t Nd = a.n_docs;
   const int64_t d0 = Nd * sl / ns, d1 = Nd * (sl + 1) / ns;
-  const char* Db = (const char*)a.D;
-  float acc[EPC];
-#pragma unroll
-  for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-  // round r: lane c of a token loads the index and weight of document k0 + c
-  // and turns them into a row of the slice (row 0 and weight 0 when the
-  // document has no valid row for this token); every lane of the token then
-  // takes all U of them by lane swaps and gathers with no further checks
-  const char* Ds = Db + d0 * a.Ld * (int64_t)G::kRowBytes;
-  auto fetch_idx = [&](int64_t k0, int& row, float& w) {
+  // the slice's rows, read through a buffer descriptor (the plan keeps a
+  // slice below 2^32 bytes)
+  const char* Ds = (const char*)a.D + d0 * a.Ld * (int64_t)G::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(Ds, (uint32_t)((d1 - d0) * a.Ld * G::kRowBytes));
+  const int32_t* am = a.argmax + q * Nd * a.Lq + i;     // + d * Lq
+  const float* gq = a.g + q * Nd;
+  const uint32_t my_chunk = (uint32_t)c * 16u;
+  auto prep = [&](int64_t k0, uint32_t& off, float& w) {
     const int64_t d = k0 + c;
-    row = 0;
+    off = 0;
     w = 0.0f;
-    if (c < U && d < d1) {
-      const int64_t p = q * Nd + d;
-      const int j = a.argmax[p * a.Lq + i];
+    if (c < R && d < d1) {
+      const int j = am[d * a.Lq];
       if (j >= 0 && j < a.Ld) {
-        row = (int)((d - d0) * a.Ld + j);
-        w = a.g[p];
+        off = (uint32_t)(((d - d0) * a.Ld + j) * G::kRowBytes);
+        w = gq[d];
       }
     }
   };
-  int rn;
+  float acc[EPC];
+#pragma unroll
+  for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
+  uint32_t on;
   float wn;
-  fetch_idx(d0, rn, wn);
-  for (int64_t k0 = d0; k0 < d1; k0 += U) {
-    const int rc = rn;
+  prep(d0, on, wn);
+  for (int64_t k0 = d0; k0 < d1; k0 += R) {
+    const uint32_t oc = on;
     const float wc = wn;
-    fetch_idx(k0 + U, rn, wn);             // next round's indices in flight
-    u32x4 ch[U];
-    float gg[U];
+    prep(k0 + R, on, wn);                  // next round's lookups in flight
+    u32x4 ch[R];
+    float gg[R];
+    static_for<R>([&](auto u) {
+      // a looked-up offset is the row's start; add this lane's chunk
+      const uint32_t o = (uint32_t)grp_bcast<CPR, u>((int)oc, base_lane);
+      ch[u] = ld_buf_16(rs, o + my_chunk);
+      gg[u] = grp_bcast_f<CPR, u>(wc, base_lane);
+    });
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = __shfl(rc, base_lane + u);
-      gg[u] = __shfl(wc, base_lane + u);
-      ch[u] = ld_global_16(Ds + (int64_t)row * G::kRowBytes + c * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < R; ++u) {
       float f[EPC];
       chunk_to_float<E>(ch[u], f);
 #pragma unroll
@@ -191,7 +241,7 @@ __global__ __launch_bounds__(256) void gradq_xcd_kernel(BwdArgs a) {
     }
   }
   if (!tok_ok) return;
-  float* out = a.gq_part + ((int64_t)sl * n_tok + qi) * DIM + c * EPC;
+  float* out = (ns > 1 ? a.gq_part + (int64_t)sl * n_tok * DIM : a.gQ) + qi * DIM + c * EPC;
 #pragma unroll
   for (int k = 0; k < EPC; k += 4)
     *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
@@ -489,27 +539,35 @@ __global__ __launch_bounds__(256) void gradd_rows_group_kernel(BwdArgs a, int rp
   }
 }
 // ---------------------------------------------------------------------------
-// grad_D, all-pairs, fused: workgroup (document e, split s) of kFzThreads.
+// grad_D, all-pairs, sorted: workgroup (document e, split s) of kGsThreads.
 //
-//  1. keys: the row a(q,e,i) of every hit h = q*Lq + i (0xffff for none), and
-//     (the row histograms of each sorting wave come with the ranks of step 3);
-//  2. row starts (exclusive scan) and per-wave cursors; the document's valid
-//     hits are cut into fz_split equal shares at row boundaries, and this
-//     workgroup owns the rows [c0, c1) of share s;
-//  3. stable placement: sorting wave w walks its contiguous hit range in
-//     64-hit chunks; a hit's slot is its row's cursor plus its rank among the
-//     chunk's hits of the same row, so the sorted list is ordered by row,
-//     then by h;
+//  1. sorting wave w takes the hits [w*Hw, (w+1)*Hw) in chunks of 64: the key
+//     of hit h = q*Lq + i is its row a(q,e,i) (none for masked tokens).  The
+//     lanes of a chunk holding the same row find each other through an LDS
+//     word per row that each ORs its lane bit into (OR is order-free, so the
+//     word is exact; long documents use ballots over the key bits instead); a
+//     hit's rank is the number of such lanes below it, and the last of them
+//     adds their count to the wave's row histogram.  Key, rank and count are
+//     kept per hit;
+//  2. row starts (exclusive scan over rows of all waves' counts) and per-wave
+//     cursors; the document's hits are cut into gs_split equal shares at row
+//     boundaries and this workgroup owns the rows [c0, c1) of share s; its
+//     rows without hits are written as zeros now;
+//  3. placement in chunk order: slot = the wave's cursor of the row + rank,
+//     so the sorted list is ordered by row, then by h (a stable sort);
 //  4. the sorted hits of [c0, c1) are cut into NG equal ranges, one per lane
-//     group of CPR lanes (16 bytes of the row each).  A group adds g * Q[h]
-//     over its range in sorted order and writes each row it holds whole; a row
-//     cut by a range boundary leaves a partial in LDS, and after a barrier the
-//     group where that row starts adds the later groups' partials in group
-//     order.  Rows without hits are written as zeros.
+//     group of CPR lanes (16 bytes of the row each).  A group takes R hits per
+//     round: lane u of the group reads sorted entry u and prepares its Q-row
+//     offset, weight g[q, e] and row; the group's lanes gather the R rows with
+//     those values broadcast from lane u and add g * Q[h] in sorted order.  A
+//     round inside one row (the usual case) needs no row checks; a row that
+//     ends is stored whole, kept as the range's head (begun in an earlier
+//     range) or, at the range's end, left as a partial in LDS, and after a
+//     barrier the group where that row starts adds the later groups' partials
+//     in group order.
 // The sums depend only on the sorted list, so results are bitwise stable.
 // ---------------------------------------------------------------------------
-constexpr int kFzWaves = kFzThreads / kWave;
-constexpr int kFzMaxChunks = kFzMaxHitsPerWave / 64;   // 64-hit chunks per sorting wave
+constexpr int kGsWaves = kGsThreads / kWave;
 
 // h / Lq for 0 <= h < 2^16 and 1 <= Lq <= 2^16, with magic = ceil(2^32 / Lq):
 // the rounding error of the product is below 2^-16 <= 1/Lq, so the floor is exact.
@@ -517,103 +575,98 @@ __device__ __forceinline__ int div_lq(int h, uint64_t magic) {
   return (int)(((uint64_t)(uint32_t)h * magic) >> 32);
 }
 
+// rank of this lane among the valid lanes holding the same key, and their
+// count (keys of `bits` bits; every lane takes part in the ballots)
+__device__ __forceinline__ void match_rank(int key, bool valid, int bits, uint64_t below,
+                                           int& rank, int& count) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = valid && ((key >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    same &= bit ? bb : ~bb;
+  }
+  rank = __popcll(same & below);
+  count = __popcll(same);
+}
+
 template <Elem E, int DIM>
-__global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4))) void gradd_fused_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
   using G = Geo<E, DIM>;
   constexpr int EPC = ElemInfo<E>::kPerChunk;
   constexpr int CPR = G::kCPR;
-  constexpr int NG = kFzThreads / CPR;     // lane groups
-  constexpr int B = 6;                     // hits per batch
+  constexpr int NG = kGsThreads / CPR;     // lane groups
+  constexpr int R = CPR < 16 ? CPR : 16;   // hits per round (one prepared per lane)
   constexpr int F4 = DIM / 4;              // float4 per gradient row
-  extern __shared__ __attribute__((aligned(16))) char fz_smem[];
-  char* smem = fz_smem;
-  int32_t* start = reinterpret_cast<int32_t*>(smem + a.fz_off_start);     // [Ld + 1]
-  int32_t* cnt = reinterpret_cast<int32_t*>(smem + a.fz_off_cnt);         // [SW][Ld]
-  uint32_t* sorted = reinterpret_cast<uint32_t*>(smem + a.fz_off_sorted); // [H]: row << 16 | h
-  float* gl = reinterpret_cast<float*>(smem + a.fz_off_gl);               // [Nq]
-  uint16_t* keys = reinterpret_cast<uint16_t*>(smem + a.fz_off_union);    // [H] (steps 1-3)
-  uint64_t* masks = reinterpret_cast<uint64_t*>(smem + a.fz_off_masks);   // [SW][Ld] (step 3a)
-  float* part = reinterpret_cast<float*>(smem + a.fz_off_union);          // [NG][2][DIM] (step 4)
-  __shared__ int wtot[kFzWaves];
+  constexpr uint32_t kNoKey = 0xffffu;
+  extern __shared__ __attribute__((aligned(16))) char gs_smem[];
+  uint32_t* sorted = reinterpret_cast<uint32_t*>(gs_smem + a.gs_off_sorted);  // [H]: row << 16 | h
+  int32_t* start = reinterpret_cast<int32_t*>(gs_smem + a.gs_off_start);      // [Ld + 1]
+  float* gl = reinterpret_cast<float*>(gs_smem + a.gs_off_gl);                // [Nq]
+  uint32_t* keys = reinterpret_cast<uint32_t*>(gs_smem + a.gs_off_keys);      // [H] (steps 1-3)
+  int32_t* hist = reinterpret_cast<int32_t*>(gs_smem + a.gs_off_hist);        // [SW][Ld] (steps 1-3)
+  unsigned long long* masks =
+      reinterpret_cast<unsigned long long*>(gs_smem + a.gs_off_masks);        // [SW][Ld] (step 1)
+  float* part = reinterpret_cast<float*>(gs_smem + a.gs_off_part);            // [NG][2][DIM] (step 4)
+  __shared__ int wtot[kGsWaves];
   __shared__ int cut[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = a.fz_split;
+  const int split = a.gs_split;
   const int64_t e = blockIdx.x / split;
   const int s = (int)(blockIdx.x - e * split);
   const int Ld = (int)a.Ld, H = (int)a.H, Lq = (int)a.Lq, Nq = (int)a.Nq;
-  const int SW = a.fz_sw;
+  const int SW = a.gs_sw;
   const int Hw = ((H + SW * 64 - 1) / (SW * 64)) * 64;   // hits per sorting wave
   const int64_t Nd = a.n_docs;
+  const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  const bool use_masks = a.gs_masks != 0;
+  float* __restrict__ gD_doc = a.gD + e * (int64_t)Ld * DIM;
 
-  // 0. clear the histograms and match masks; this document's upstream grads
-  for (int k = tid; k < SW * Ld; k += kFzThreads) {
-    cnt[k] = 0;
-    masks[k] = 0ull;
+  // 0. clear the histograms and match words; this document's upstream grads
+  for (int k = tid; k < SW * Ld; k += kGsThreads) {
+    hist[k] = 0;
+    if (use_masks) masks[k] = 0ull;
   }
-  for (int q = tid; q < Nq; q += kFzThreads) gl[q] = a.g[(int64_t)q * Nd + e];
-
-  // 1. keys: the row of every hit (16 independent argmax loads per thread)
-  constexpr int UL = 16;
-  for (int hb = tid; hb < H; hb += kFzThreads * UL) {
-    int jj[UL];
-#pragma unroll
-    for (int u = 0; u < UL; ++u) {
-      const int h = hb + u * kFzThreads;
-      jj[u] = -1;
-      if (h < H) {
-        const int q = div_lq(h, a.lq_magic);
-        const int i = h - q * Lq;
-        jj[u] = a.argmax[((int64_t)q * Nd + e) * Lq + i];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UL; ++u) {
-      const int h = hb + u * kFzThreads;
-      if (h < H) keys[h] = (jj[u] >= 0 && jj[u] < Ld) ? (uint16_t)jj[u] : (uint16_t)0xffff;
-    }
-  }
+  for (int q = tid; q < Nq; q += kGsThreads) gl[q] = a.g[(int64_t)q * Nd + e];
   __syncthreads();
 
-  // 3a. sorting wave w takes hits [w*Hw, (w+1)*Hw) in chunks of 64.  The lanes
-  // of a chunk holding the same row find each other through an LDS mask that
-  // each ORs its lane bit into (OR is order-free, so the mask is exact); a
-  // hit's rank is the number of such lanes below it.  The last of them adds
-  // the chunk's count to the wave's row histogram.
-  const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  // per chunk: row (16 bits, 0xffff none) | rank << 16 | count << 23
-  int rc[kFzMaxChunks];
+  // 1. keys, ranks inside each 64-hit chunk, per-wave row histograms
   const int h0 = min(wave * Hw, H), h1 = min(h0 + Hw, H);
   if (wave < SW) {
-    int* hist = cnt + wave * Ld;
-    unsigned long long* msk = reinterpret_cast<unsigned long long*>(masks + wave * Ld);
-    constexpr int CG = 4;                        // chunks whose LDS traffic is in flight together
+    int* hw = hist + wave * Ld;
+    unsigned long long* mw = masks + wave * Ld;
+    constexpr int UL = 8;                        // chunks whose argmax loads are in flight together
+    for (int hb = h0; hb < h1; hb += 64 * UL) {
+      int jj[UL];
 #pragma unroll
-    for (int g0 = 0; g0 < kFzMaxChunks; g0 += CG) {
-      if (h0 + g0 * 64 >= h1) break;
-      int jj[CG];
-      uint64_t same[CG];
-#pragma unroll
-      for (int u = 0; u < CG; ++u) {
-        const int h = h0 + (g0 + u) * 64 + lane;
-        jj[u] = h < h1 ? (int)keys[h] : 0xffff;
-      }
-      // OR, read back and clear, chunk after chunk: LDS runs a wave's
-      // operations in order, so no wait is needed between them
-#pragma unroll
-      for (int u = 0; u < CG; ++u) {
-        const bool v = jj[u] != 0xffff;
-        if (v) atomicOr(&msk[jj[u]], 1ull << lane);
-        same[u] = v ? (uint64_t)msk[jj[u]] : 0ull;
-        if (v) msk[jj[u]] = 0ull;
+      for (int u = 0; u < UL; ++u) {
+        const int h = hb + 64 * u + lane;
+        jj[u] = (int)kNoKey;
+        if (h < h1) {
+          const int q = div_lq(h, a.lq_magic);
+          const int i = h - q * Lq;
+          const int j = a.argmax[((int64_t)q * Nd + e) * Lq + i];
+          if (j >= 0 && j < Ld) jj[u] = j;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < CG; ++u) {
-        const bool v = jj[u] != 0xffff;
-        const int rank = __popcll(same[u] & below);
-        const int count = __popcll(same[u]);
-        rc[g0 + u] = jj[u] | (rank << 16) | (count << 23);
-        if (v && rank == count - 1) atomicAdd(&hist[jj[u]], count);
+      for (int u = 0; u < UL; ++u) {
+        if (hb + 64 * u >= h1) break;            // wave-uniform
+        const int h = hb + 64 * u + lane;
+        const bool v = jj[u] != (int)kNoKey;
+        int rank, count;
+        if (use_masks) {
+          // OR, read back and clear: LDS runs one wave's operations in order
+          if (v) atomicOr(&mw[jj[u]], 1ull << lane);
+          const uint64_t same = v ? (uint64_t)mw[jj[u]] : 0ull;
+          if (v) mw[jj[u]] = 0ull;
+          rank = __popcll(same & below);
+          count = __popcll(same);
+        } else {
+          match_rank(jj[u], v, a.key_bits, below, rank, count);
+        }
+        if (h < h1) keys[h] = (uint32_t)jj[u] | ((uint32_t)rank << 16) | ((uint32_t)count << 22);
+        if (v && rank == count - 1) atomicAdd(&hw[jj[u]], count);
       }
     }
   }
@@ -621,11 +674,11 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
   // 2. row starts and per-wave cursors (each thread scans a segment of rows)
   {
-    const int seg = (Ld + kFzThreads - 1) / kFzThreads;
+    const int seg = (Ld + kGsThreads - 1) / kGsThreads;
     const int lo = min(tid * seg, Ld), hi = min(lo + seg, Ld);
     int local = 0;
     for (int j = lo; j < hi; ++j)
-      for (int w = 0; w < SW; ++w) local += cnt[w * Ld + j];
+      for (int w = 0; w < SW; ++w) local += hist[w * Ld + j];
     int incl = local;
 #pragma unroll
     for (int k = 1; k < 64; k <<= 1) {
@@ -639,14 +692,14 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4)))
     for (int j = lo; j < hi; ++j) {
       start[j] = base;
       for (int w = 0; w < SW; ++w) {
-        const int c = cnt[w * Ld + j];
-        cnt[w * Ld + j] = base;
-        base += c;
+        const int cnt = hist[w * Ld + j];
+        hist[w * Ld + j] = base;
+        base += cnt;
       }
     }
     if (tid == 0) {
       int tot = 0;
-      for (int w = 0; w < kFzWaves; ++w) tot += wtot[w];
+      for (int w = 0; w < kGsWaves; ++w) tot += wtot[w];
       start[Ld] = tot;
     }
   }
@@ -670,89 +723,109 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4)))
   __syncthreads();
   const int c0 = cut[0], c1 = cut[1];
 
-  // 3b. placement in chunk order: slot = the wave's cursor of the row + rank;
+  // rows of [c0, c1) without hits are zeros: stored now, so that the writes
+  // drain while the hits are placed and summed
+  {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = tid; k < (c1 - c0) * F4; k += kGsThreads) {
+      const int row = c0 + k / F4, f = k - (k / F4) * F4;
+      if (start[row] == start[row + 1])
+        *reinterpret_cast<float4*>(gD_doc + (int64_t)row * DIM + 4 * f) = z;
+    }
+  }
+
+  // 3. placement in chunk order: slot = the wave's cursor of the row + rank;
   // the sorted list is ordered by row, then by h.  Only rows in [c0, c1).
   if (wave < SW) {
-    int* cur = cnt + wave * Ld;
-#pragma unroll
-    for (int ch = 0; ch < kFzMaxChunks; ++ch) {
-      if (h0 + ch * 64 >= h1) break;
-      const int h = h0 + ch * 64 + lane;
-      const int j = rc[ch] & 0xffff;
-      const bool v = j != 0xffff;
-      const int rank = (rc[ch] >> 16) & 0x7f, count = rc[ch] >> 23;
-      const int pos = v ? cur[j] : 0;
+    int* cur = hist + wave * Ld;
+    for (int hb = h0; hb < h1; hb += 64) {
+      const int h = hb + lane;
+      const uint32_t kr = h < h1 ? keys[h] : kNoKey;
+      const int j = (int)(kr & 0xffffu);
+      const int rank = (int)((kr >> 16) & 0x3fu), count = (int)(kr >> 22);
+      const bool mine = j != (int)kNoKey && j >= c0 && j < c1;
+      const int pos = mine ? cur[j] : 0;
       __asm__ volatile("" ::: "memory");
-      if (v && j >= c0 && j < c1) sorted[pos + rank] = ((uint32_t)j << 16) | (uint32_t)h;
-      if (v && rank == count - 1) cur[j] = pos + count;
+      if (mine) sorted[pos + rank] = ((uint32_t)j << 16) | (uint32_t)h;
+      if (mine && rank == count - 1) cur[j] = pos + count;
     }
   }
   __syncthreads();
 
-  // 4. row sums over equal shares of the sorted hits.  Inside the hit loop a
-  // finished row is either whole (stored to grad_D) or the range's first row
-  // begun in an earlier range (kept in registers); partials reach LDS only
-  // after the loop, so the loop holds no LDS stores and one kind of global
-  // store, and the next batch's rows are in flight while a batch is summed.
+  // 4. row sums over equal shares of the sorted hits
   const int H0 = start[c0], H1 = start[c1];
   const int grp = tid / CPR, c = tid - grp * CPR;
+  const int base_lane = lane - c;
   auto range_lo = [&](int k) { return H0 + (int)((int64_t)(H1 - H0) * k / NG); };
   const int lo = range_lo(grp), hi = range_lo(grp + 1);
-  float* __restrict__ gD_doc = a.gD + e * (int64_t)Ld * DIM;
-  const char* Qb = (const char*)a.Q;
+  const __amdgpu_buffer_rsrc_t qrs = buf_rsrc(a.Q, (uint32_t)((int64_t)Nq * Lq * G::kRowBytes));
+  const uint32_t my_chunk = (uint32_t)c * 16u;
   float acc[EPC], head[EPC];
 #pragma unroll
   for (int k = 0; k < EPC; ++k) acc[k] = head[k] = 0.0f;
   int cur_row = lo < hi ? (int)(sorted[lo] >> 16) : -1;
   bool in_head = lo < hi && start[cur_row] < lo;   // first row began in an earlier range
   bool have_head = false;
-  auto fetch = [&](int p0, uint32_t (&en)[B], u32x4 (&cq)[B], float (&gq)[B]) {
+  auto store_row = [&](int row, const float (&v)[EPC]) {
+    float* out = gD_doc + (int64_t)row * DIM + c * EPC;
 #pragma unroll
-    for (int m = 0; m < B; ++m) en[m] = (p0 + m < hi) ? sorted[p0 + m] : 0u;
-#pragma unroll
-    for (int m = 0; m < B; ++m) {
-      const int h = (int)(en[m] & 0xffffu);    // 0 past the range: a valid row, weight 0
-      cq[m] = ld_global_16(Qb + (int64_t)h * G::kRowBytes + c * 16);
-      gq[m] = (p0 + m < hi) ? gl[div_lq(h, a.lq_magic)] : 0.0f;
-    }
+    for (int k = 0; k < EPC; k += 4)
+      *reinterpret_cast<float4*>(out + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
   };
-  auto consume = [&](int p0, const uint32_t (&en)[B], const u32x4 (&cq)[B], const float (&gq)[B]) {
+  // a row ended inside the range: the head (begun earlier) is kept, any
+  // other row is whole and stored
+  auto end_row = [&]() {
+    if (in_head) {
 #pragma unroll
-    for (int m = 0; m < B; ++m) {
-      const int row = (p0 + m < hi) ? (int)(en[m] >> 16) : cur_row;
-      if (row != cur_row) {
-        if (in_head) {
+      for (int k = 0; k < EPC; ++k) head[k] = acc[k];
+      have_head = true;
+      in_head = false;
+    } else {
+      store_row(cur_row, acc);
+    }
 #pragma unroll
-          for (int k = 0; k < EPC; ++k) head[k] = acc[k];
-          have_head = true;
-          in_head = false;
-        } else {
-          float* out = gD_doc + (int64_t)cur_row * DIM + c * EPC;
-#pragma unroll
-          for (int k = 0; k < EPC; k += 4)
-            *reinterpret_cast<float4*>(out + k) =
-                make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
-        }
-#pragma unroll
-        for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-        cur_row = row;
-      }
+    for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
+  };
+  for (int p = lo; p < hi; p += R) {
+    // lane u (< R) of the group prepares sorted entry p + u; entries past the
+    // range repeat the range's last entry with weight 0 (same row, no effect)
+    int row_c = 0;
+    uint32_t qoff_c = 0;
+    float g_c = 0.0f;
+    if (c < R) {
+      const int pe = min(p + c, hi - 1);
+      const uint32_t ent = sorted[pe];
+      const int h = (int)(ent & 0xffffu);
+      row_c = (int)(ent >> 16);
+      qoff_c = (uint32_t)h * (uint32_t)G::kRowBytes;
+      g_c = p + c < hi ? gl[div_lq(h, a.lq_magic)] : 0.0f;
+    }
+    u32x4 ch[R];
+    static_for<R>([&](auto u) {
+      const uint32_t o = (uint32_t)grp_bcast<CPR, u>((int)qoff_c, base_lane);
+      ch[u] = ld_buf_16(qrs, o + my_chunk);
+    });
+    // weights and rows are broadcast where they are used (few live registers)
+    auto add = [&](const u32x4& x, float w) {
       float f[EPC];
-      chunk_to_float<E>(cq[m], f);
+      chunk_to_float<E>(x, f);
 #pragma unroll
-      for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gq[m], f[k], acc[k]);
+      for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(w, f[k], acc[k]);
+    };
+    // entries are sorted by row: the round stays in the current row iff its
+    // last entry does
+    if (__ballot(grp_bcast<CPR, R - 1>(row_c, base_lane) != cur_row) == 0ull) {
+      static_for<R>([&](auto u) { add(ch[u], grp_bcast_f<CPR, u>(g_c, base_lane)); });
+    } else {
+      static_for<R>([&](auto u) {
+        const int r = grp_bcast<CPR, u>(row_c, base_lane);
+        if (r != cur_row) {
+          end_row();
+          cur_row = r;
+        }
+        add(ch[u], grp_bcast_f<CPR, u>(g_c, base_lane));
+      });
     }
-  };
-  // two batches per step: the second is in flight while the first is summed
-  // (no loads are carried across steps, so none is waited for early)
-  for (int p0 = lo; p0 < hi; p0 += 2 * B) {
-    uint32_t ea[B], eb[B];
-    u32x4 ca[B], cb[B];
-    float ga[B], gb[B];
-    fetch(p0, ea, ca, ga);
-    fetch(p0 + B, eb, cb, gb);
-    consume(p0, ea, ca, ga);
-    consume(p0 + B, eb, cb, gb);
   }
   // the range's last row: whole, a tail (continues in later ranges), or the
   // head itself (the range lies inside one row)
@@ -769,10 +842,7 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4)))
       for (int k = 0; k < EPC; k += 4)
         *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
     } else {
-      float* out = gD_doc + (int64_t)cur_row * DIM + c * EPC;
-#pragma unroll
-      for (int k = 0; k < EPC; k += 4)
-        *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+      store_row(cur_row, acc);
     }
   }
   if (have_head) {
@@ -798,17 +868,7 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(4)))
         for (int k = 0; k < EPC; ++k) acc[k] += pp[k];
       }
     }
-    float* out = gD_doc + (int64_t)tail_row * DIM + c * EPC;
-#pragma unroll
-    for (int k = 0; k < EPC; k += 4)
-      *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
-  }
-  // rows of [c0, c1) without hits
-  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = tid; k < (c1 - c0) * F4; k += kFzThreads) {
-    const int row = c0 + k / F4, f = k - (k / F4) * F4;
-    if (start[row] == start[row + 1])
-      *reinterpret_cast<float4*>(gD_doc + (int64_t)row * DIM + 4 * f) = z;
+    store_row(tail_row, acc);
   }
 }
 
@@ -944,12 +1004,12 @@ static hipError_t launch_gradq(const BwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
   constexpr int CPR = G::kCPR;
   constexpr int TPB = 256 / CPR;
-  if (a.gq_slices > 1) {
+  if (a.gq_ap) {
     const int64_t n_tok = a.Nq * a.Lq;
-    hipLaunchKernelGGL((gradq_xcd_kernel<E, DIM>), dim3((unsigned)(a.gq_slices * cdiv(n_tok, TPB))),
+    hipLaunchKernelGGL((gradq_ap_kernel<E, DIM>), dim3((unsigned)(a.gq_slices * cdiv(n_tok, TPB))),
                        dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.gq_slices == 1) return e;
     const int64_t n4 = n_tok * DIM / 4;
     hipLaunchKernelGGL(gradq_reduce_kernel, dim3((unsigned)cdiv(n4, 256)), dim3(256), 0, s,
                        reinterpret_cast<const float4*>(a.gq_part), a.gq_slices, n4,
@@ -962,18 +1022,18 @@ static hipError_t launch_gradq(const BwdArgs& a, hipStream_t s) {
 }
 
 template <Elem E, int DIM>
-static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t fz_lds, hipStream_t s) {
+static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t gs_lds, hipStream_t s) {
   using G = Geo<E, DIM>;
   constexpr int CPR = G::kCPR;
   hipError_t e;
-  if (mode == kGdFused) {
-    if (fz_lds > 65536) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gradd_fused_kernel<E, DIM>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)fz_lds);
+  if (mode == kGdSorted) {
+    if (gs_lds > 65536) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gradd_sorted_kernel<E, DIM>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)gs_lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gradd_fused_kernel<E, DIM>), dim3((unsigned)(a.n_docs * a.fz_split)),
-                       dim3(kFzThreads), fz_lds, s, a);
+    hipLaunchKernelGGL((gradd_sorted_kernel<E, DIM>), dim3((unsigned)(a.n_docs * a.gs_split)),
+                       dim3(kGsThreads), gs_lds, s, a);
     return hipGetLastError();
   }
   if (mode == kGdPairs) {
@@ -1009,7 +1069,7 @@ static hipError_t launch_grads(const BwdPlan& p, const BwdArgs& a, bool want_q, 
     hipError_t e = launch_gradq<E, DIM>(a, s);
     if (e != hipSuccess) return e;
   }
-  if (want_d) return launch_gradd<E, DIM>(a, p.gd_mode, p.fz_lds, s);
+  if (want_d) return launch_gradd<E, DIM>(a, p.gd_mode, p.gs_lds, s);
   return hipSuccess;
 }
 
@@ -1058,15 +1118,18 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
   a.layout = f.layout;
   a.key_bits = p.key_bits;
   a.gq_slices = p.gq_slices;
-  a.fz_sw = p.fz_sw;
-  a.fz_split = p.fz_split;
+  a.gq_ap = p.gq_ap ? 1 : 0;
+  a.gs_sw = p.gs_sw;
+  a.gs_split = p.gs_split;
   a.gd_parts = p.gd_parts;
-  a.fz_off_start = p.fz_off_start;
-  a.fz_off_cnt = p.fz_off_cnt;
-  a.fz_off_sorted = p.fz_off_sorted;
-  a.fz_off_gl = p.fz_off_gl;
-  a.fz_off_union = p.fz_off_union;
-  a.fz_off_masks = p.fz_off_masks;
+  a.gs_off_sorted = p.gs_off_sorted;
+  a.gs_off_start = p.gs_off_start;
+  a.gs_off_gl = p.gs_off_gl;
+  a.gs_off_keys = p.gs_off_keys;
+  a.gs_off_hist = p.gs_off_hist;
+  a.gs_off_masks = p.gs_off_masks;
+  a.gs_off_part = p.gs_off_part;
+  a.gs_masks = p.gs_masks;
   a.lq_magic = ((uint64_t(1) << 32) + (uint64_t)f.Lq - 1) / (uint64_t)f.Lq;
   a.Nq = f.Nq;
   a.Lq = f.Lq;

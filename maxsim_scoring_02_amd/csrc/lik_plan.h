@@ -47,7 +47,7 @@ struct FwdPlan {
 // grad_D strategies
 enum GdMode : int {
   kGdSort = 0,    // sort kernel + row kernel through the workspace (any shape)
-  kGdFused = 1,   // all-pairs: one fused kernel per document, sort in LDS
+  kGdSorted = 1,  // all-pairs: per document, one workgroup sorts its hits in LDS and sums them
   kGdPairs = 2    // pairwise / kd: waves per document stream contiguous row ranges
 };
 // pairwise / kd grad_D: at least this many waves per document, and enough
@@ -55,8 +55,8 @@ enum GdMode : int {
 constexpr int kGdPairsMinParts = 4;
 constexpr int64_t kGdPairsWaves = 65536;
 constexpr int64_t kGdPairsMinRows = 64;   // rows a wave streams, at least
-constexpr int kFzThreads = 512;        // threads of the fused grad_D workgroup
-constexpr int kFzMaxHitsPerWave = 2048; // hits one sorting wave of it ranks
+constexpr int kGsThreads = 1024;       // threads of the sorted grad_D workgroup
+constexpr int kGsLdsMax = 160 * 1024;  // LDS of one CU
 constexpr int kPairsMaxLq = 256;   // longest query of the pairs grad_D kernel
 constexpr int64_t kGqSliceMinDocs = 64;
 
@@ -67,11 +67,16 @@ struct BwdPlan {
   int key_bits = 1;
   int gd_mode = kGdSort;
   int gd_parts = kGdPairsMinParts;   // pairwise / kd grad_D: waves per document
-  // fused grad_D: sorting waves, workgroups per document, dynamic LDS layout
-  int fz_sw = 0, fz_split = 1;
-  int fz_off_start = 0, fz_off_cnt = 0, fz_off_sorted = 0, fz_off_gl = 0, fz_off_union = 0,
-      fz_off_masks = 0;
-  size_t fz_lds = 0;
+  // sorted grad_D: sorting waves, workgroups per document, dynamic LDS layout
+  // (sorted hits, row starts, the document's upstream grads, then a region
+  // that holds the keys and row histograms while sorting and the partial rows
+  // while summing)
+  int gs_sw = 0, gs_split = 1;
+  int gs_masks = 0;         // ranks from LDS match masks (else from ballots over the key bits)
+  int gs_off_sorted = 0, gs_off_start = 0, gs_off_gl = 0, gs_off_keys = 0, gs_off_hist = 0,
+      gs_off_masks = 0, gs_off_part = 0;
+  size_t gs_lds = 0;
+  bool gq_ap = false;       // all-pairs grad_Q by document rounds (gradq_ap_kernel)
   int gq_slices = 1;        // >1: grad_Q gathered per document slice, then reduced
   size_t off_argmax = 0, off_scores = 0, off_sorted = 0, off_sorted_g = 0, off_roff = 0, off_fwd = 0,
          off_gq_part = 0, total = 0;
@@ -235,42 +240,48 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
   b.key_bits = bits;
   // grad_D strategy
   const int esize = elem == 2 ? 4 : 2;
-  if (layout == kAllPairs && b.H <= 65536 && Ld <= 65535 && Lq > 0 && Ld > 0) {
+  const int64_t q_bytes = f.Nq * Lq * dim * esize;
+  if (layout == kAllPairs && b.H <= 65535 && Ld <= 65535 && Lq > 0 && Ld > 0 &&
+      q_bytes < (int64_t(1) << 32)) {
+    // one workgroup sorts a document's hits by row (stable, in LDS) and its
+    // lane groups (one 16-byte chunk of a row per lane) sum them
     const size_t cpr = (size_t)dim * esize / 16;
-    const size_t ng = kFzThreads / cpr;
+    const size_t ng = kGsThreads / cpr;
     const size_t part = ng * 2 * (size_t)dim * 4;
-    const size_t keys = align16((size_t)b.H * 2);
-    const size_t start = align16((size_t)(Ld + 1) * 4);
     const size_t sorted = align16((size_t)b.H * 4);
+    const size_t start = align16((size_t)(Ld + 1) * 4);
     const size_t gl = align16((size_t)f.Nq * 4);
-    // prefer two workgroups per CU (<= 80 KiB), else one (<= 150 KiB)
-    const size_t limits[2] = {80 * 1024, 150 * 1024};
-    for (int li = 0; li < 2 && b.gd_mode == kGdSort; ++li) {
-      for (int sw = kFzThreads / 64; sw >= 1; sw /= 2) {
-        if (cdiv(b.H, sw) > kFzMaxHitsPerWave) break;
-        const size_t cnt = align16((size_t)sw * Ld * 4);
-        const size_t masks = (size_t)sw * Ld * 8;
-        const size_t ph3 = keys + masks;              // keys and masks, then the partials
-        const size_t uni = part > ph3 ? part : ph3;
-        const size_t tot = start + cnt + sorted + gl + uni;
-        if (tot <= limits[li]) {
-          b.gd_mode = kGdFused;
-          b.fz_sw = sw;
-          b.fz_off_start = 0;
-          b.fz_off_cnt = (int)start;
-          b.fz_off_sorted = (int)(start + cnt);
-          b.fz_off_gl = (int)(start + cnt + sorted);
-          b.fz_off_union = (int)(start + cnt + sorted + gl);
-          b.fz_off_masks = (int)(start + cnt + sorted + gl + keys);
-          b.fz_lds = tot;
+    const size_t keys = align16((size_t)b.H * 4);   // key | rank << 16 | count << 22 per hit
+    const int64_t chunks = cdiv(b.H, 64);
+    // ranks from per-wave LDS match masks (one 64-bit word per row) when they
+    // fit, else from ballots over the key bits (long documents)
+    for (int use_masks = 1; use_masks >= 0 && b.gd_mode != kGdSorted; --use_masks) {
+      for (int sw = kGsThreads / 64; sw >= 1; sw /= 2) {
+        if (sw > 1 && sw > chunks) continue;        // no more sorting waves than 64-hit chunks
+        const size_t hist = align16((size_t)sw * Ld * 4);
+        const size_t masks = use_masks ? (size_t)sw * Ld * 8 : 0;
+        const size_t uni = part > keys + hist + masks ? part : keys + hist + masks;
+        const size_t tot = sorted + start + gl + uni;
+        if (tot <= (size_t)kGsLdsMax) {
+          b.gd_mode = kGdSorted;
+          b.gs_sw = sw;
+          b.gs_masks = use_masks;
+          b.gs_off_sorted = 0;
+          b.gs_off_start = (int)sorted;
+          b.gs_off_gl = (int)(sorted + start);
+          b.gs_off_keys = (int)(sorted + start + gl);
+          b.gs_off_hist = (int)(sorted + start + gl + keys);
+          b.gs_off_masks = (int)(sorted + start + gl + keys + hist);
+          b.gs_off_part = (int)(sorted + start + gl);
+          b.gs_lds = tot;
           break;
         }
       }
     }
-    if (b.gd_mode == kGdFused) {
-      // enough workgroups to give every CU two
-      int64_t sp = cdiv(512, f.n_docs);
-      b.fz_split = (int)(sp < 1 ? 1 : (sp > 8 ? 8 : sp));
+    if (b.gd_mode == kGdSorted) {
+      // every CU holds one such workgroup: split documents until about 256 run
+      int64_t sp = cdiv(256, f.n_docs);
+      b.gs_split = (int)(sp < 1 ? 1 : (sp > 8 ? 8 : sp));
     }
   } else if (layout != kAllPairs && Lq > 0 && Lq <= kPairsMaxLq && Ld > 0) {
     b.gd_mode = kGdPairs;
@@ -290,9 +301,12 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
   // slice are indexed with 32 bits.)
   const int64_t d_bytes = f.n_docs * Ld * dim * esize;
   const int slices = d_bytes <= (int64_t(128) << 20) ? 2 : 8;
+  // a slice's rows are addressed with 32-bit byte offsets
   if (layout == kAllPairs && f.n_docs >= kGqSliceMinDocs && Lq > 0 && Ld > 0 &&
-      cdiv(f.n_docs, slices) * Ld < (int64_t(1) << 31))
+      cdiv(f.n_docs, slices) * Ld * dim * esize < (int64_t(1) << 32)) {
+    b.gq_ap = true;
     b.gq_slices = slices;
+  }
 
   size_t off = 0;
   if (b.recompute && Lq > 0) {

@@ -117,8 +117,15 @@ def test_backward_rejects_invalid_arguments(L):
     assert need > 0
     assert bwd(L, argmax=None, wsb=need - 1) == LIK_ERR_INVALID_ARG
     assert "workspace too small" in L.lik_last_error().decode()
-    assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
+    # a document whose row table no longer fits in LDS goes to the workspace
+    # sort, whose row limit is 16000
+    assert bwd(L, Ld=40000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
     assert "sorts grad_D through the workspace" in L.lik_last_error().decode()
+    # 20000 rows still fit the LDS sort: the call passes every shape check and
+    # stops only at the device check here
+    assert _lib.lik_plan_value(LIK_OP_BWD, (2, 32, 3, 20000, 128), LIK_BF16, 1, "gd_mode") == 1
+    assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
+    assert "device" in L.lik_last_error().decode()
 
 
 def test_long_pairwise_and_kd_backward_pass_the_row_limit(L):

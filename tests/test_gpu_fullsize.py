@@ -33,7 +33,8 @@ OPS = {"allpairs": (_lib.LIK_OP_FWD, _lib.LIK_OP_BWD),
        "kd": (_lib.LIK_OP_KD_FWD, _lib.LIK_OP_KD_BWD)}
 FWD_KEYS = ("nb", "upw", "n_groups", "n_sb", "nchunks", "tpc", "compact", "partial", "qpw",
             "n_units")
-BWD_KEYS = ("gd_mode", "gd_parts", "fz_split", "fz_sw", "gq_slices", "recompute")
+BWD_KEYS = ("gd_mode", "gd_parts", "gs_split", "gs_sw", "gs_lds", "gq_ap", "gq_slices",
+            "recompute")
 
 
 def plan(w, backward: bool, keep_argmax: bool = True) -> dict:
@@ -194,7 +195,7 @@ def test_long_docs_backward_full_size_sampled():
     w = wl.long_docs()
     p = plan(w, backward=True)
     say(f"[plan] long-docs-bwd grad_Q slices {p['bwd_gq_slices']}, grad_D mode "
-        f"{p['bwd_gd_mode']}, fused split {p['bwd_fz_split']}")
+        f"{p['bwd_gd_mode']}, sorted split {p['bwd_gs_split']}")
     docs = _sample_long_docs(w.meta["d_len"])
     g = wl.gaussian_grad(2005, (w.Q.shape[0], w.D.shape[0])).numpy()
     keep = np.zeros(w.D.shape[0], bool)

@@ -103,16 +103,38 @@ static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
 static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, long dim) {
   BwdPlan b = make_bwd_plan(layout, elem, Nq, Lq, Nd, Ld, dim, true, true);
   if (b.fwd.Nq == 0 || b.fwd.n_docs == 0) return;
-  if (b.gd_mode == kGdFused) {
-    CHECK(b.fz_sw >= 1 && b.fz_sw <= kFzThreads / 64, "sort waves %d", b.fz_sw);
-    CHECK((b.H + b.fz_sw - 1) / b.fz_sw <= kFzMaxHitsPerWave, "hits per sort wave");
-    CHECK(b.fz_split >= 1 && b.fz_split <= 8, "split");
-    const size_t start = (size_t)(Ld + 1) * 4, sorted = (size_t)b.H * 4, gl = (size_t)Nq * 4;
-    CHECK(b.fz_off_cnt >= (int)start, "start area");
-    CHECK(b.fz_off_gl - b.fz_off_sorted >= (int)sorted, "sorted area");
-    CHECK(b.fz_off_union - b.fz_off_gl >= (int)gl, "gl area");
-    CHECK((size_t)b.fz_off_masks + (size_t)b.fz_sw * Ld * 8 <= b.fz_lds, "masks inside LDS");
-    CHECK(b.fz_lds <= 160 * 1024, "LDS %zu", b.fz_lds);
+  if (b.gd_mode == kGdSorted) {
+    // the sorted grad_D kernel: at most one sorting wave per 64-hit chunk,
+    // every LDS region inside the allocation and disjoint from the others,
+    // the keys and histograms (sorting) and the partial rows (summing) in the
+    // same region, and Q rows addressed with 32-bit offsets
+    const long esize = elem == 2 ? 4 : 2;
+    const long cpr = dim * esize / 16;
+    const size_t part = (size_t)(kGsThreads / cpr) * 2 * dim * 4;
+    CHECK(layout == kAllPairs, "sorted grad_D only for all-pairs");
+    CHECK(b.gs_sw >= 1 && b.gs_sw <= kGsThreads / 64, "sort waves %d", b.gs_sw);
+    CHECK(b.gs_sw == 1 || (long)b.gs_sw * 64 <= b.H + 63, "more sort waves than chunks");
+    CHECK(b.gs_split >= 1 && b.gs_split <= 8, "split");
+    CHECK(b.H <= 65535 && Ld <= 65535, "16-bit keys and hit numbers");
+    CHECK(Nq * Lq * dim * esize < (1L << 32), "Q offsets");
+    CHECK(b.gs_off_sorted == 0 && b.gs_off_start >= (int)(b.H * 4), "sorted area");
+    CHECK(b.gs_off_gl - b.gs_off_start >= (int)((Ld + 1) * 4), "start area");
+    CHECK(b.gs_off_keys - b.gs_off_gl >= (int)(Nq * 4), "gl area");
+    CHECK(b.gs_off_hist - b.gs_off_keys >= (int)(b.H * 4), "keys area");
+    CHECK((size_t)b.gs_off_hist + (size_t)b.gs_sw * Ld * 4 <= (size_t)b.gs_off_masks,
+          "histograms before the match words");
+    CHECK(!b.gs_masks || (size_t)b.gs_off_masks + (size_t)b.gs_sw * Ld * 8 <= b.gs_lds,
+          "match words inside LDS");
+    CHECK(b.gs_off_masks % 8 == 0, "match words aligned");
+    CHECK(b.gs_off_part == b.gs_off_keys && b.gs_off_part + part <= b.gs_lds, "partials inside LDS");
+    CHECK(b.gs_lds <= (size_t)kGsLdsMax, "LDS %zu", b.gs_lds);
+    CHECK(b.gs_off_hist % 16 == 0 && b.gs_off_part % 16 == 0, "alignment");
+  }
+  if (b.gq_ap) {
+    const long esize = elem == 2 ? 4 : 2;
+    CHECK(layout == kAllPairs && b.gq_slices >= 1, "grad_Q rounds");
+    CHECK(((b.fwd.n_docs + b.gq_slices - 1) / b.gq_slices) * Ld * dim * esize < (1L << 32),
+          "slice offsets");
   }
   if (b.gd_mode == kGdPairs) {
     // waves per document: at least the minimum, never more than the rows
