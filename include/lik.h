@@ -171,6 +171,26 @@ lik_status lik_maxsim_fwd(const void* Q, const void* D, lik_dtype dtype,
                           size_t workspace_bytes, void* stream);
 
 /*
+ * All-pairs forward that allocates nothing, for callers that cannot allocate
+ * device memory or size a workspace at call time: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels and results as lik_maxsim_fwd (bitwise), but no
+ * workspace: scratch comes from a fixed array the library holds on every
+ * device it runs on (64 MiB per device, held until the process ends; its
+ * address is resolved once per device, at the first call on that device).
+ * A call whose scratch (lik_workspace_bytes(LIK_OP_FWD, ...) with the same
+ * shapes and flags) exceeds 64 MiB returns LIK_ERR_UNSUPPORTED before any
+ * device work.  Calls that overlap on one device (other streams, other host
+ * threads) share that array and race: serialise them.  Nothing in the
+ * scratch has to start at zero, and nothing is kept between calls.
+ */
+lik_status lik_maxsim_fwd_noalloc(const void* Q, const void* D, lik_dtype dtype,
+                                  int64_t Nq, int64_t Lq, int64_t Nd, int64_t Ld,
+                                  int64_t dim, const uint8_t* q_mask,
+                                  const uint8_t* d_mask, float* scores,
+                                  int32_t* argmax, void* stream);
+
+/*
  * All-pairs backward: gradients of sum(grad_scores * scores).
  *   grad_Q[q,i,:] = sum over non-empty d of grad_scores[q,d] * D[d, a(q,d,i), :]
  *   grad_D[d,j,:] = sum over (q, valid i) with a(q,d,i) = j of

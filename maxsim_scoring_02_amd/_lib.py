@@ -49,6 +49,7 @@ SIGNATURES = {
     "lik_workspace_bytes": ([_I, _I64, _I64, _I64, _I64, _I64, _I, _I], _SZ),
     "lik_plan_value": ([_I, _I64, _I64, _I64, _I64, _I64, _I, _I, ctypes.c_char_p], _I64),
     "lik_maxsim_fwd": (_FWD_ALLPAIRS, _I),
+    "lik_maxsim_fwd_noalloc": ([_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "lik_maxsim_bwd": (_BWD_ALLPAIRS, _I),
     "lik_maxsim_pairwise_fwd": (_FWD_PAIRWISE, _I),
     "lik_maxsim_pairwise_bwd": (_BWD_PAIRWISE, _I),
@@ -174,6 +175,23 @@ def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     ws = _workspace(wsb, Q.device)
     _check(lib().lik_maxsim_fwd(_ptr(Q), _ptr(D), dt, Nq, Lq, Nd, Ld, dim, _ptr(qm), _ptr(dm),
                                 _ptr(scores), _ptr(am), _ptr(ws), wsb, _stream()))
+    return scores, am
+
+
+def lik_maxsim_fwd_noalloc(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
+    """All-pairs forward through the allocation-free entry point: the library
+    takes its scratch from a fixed per-device array (the outputs are still
+    the caller's, allocated here)."""
+    dt = _embeddings(Q, D)
+    Nq, Lq, dim = Q.shape
+    Nd, Ld, _ = D.shape
+    qm = _mask(q_mask, (Nq, Lq), Q.device)
+    dm = _mask(d_mask, (Nd, Ld), Q.device)
+    scores = torch.empty((Nq, Nd), dtype=torch.float32, device=Q.device)
+    am = (torch.empty((Nq, Nd, Lq), dtype=torch.int32, device=Q.device)
+          if keep_argmax else None)
+    _check(lib().lik_maxsim_fwd_noalloc(_ptr(Q), _ptr(D), dt, Nq, Lq, Nd, Ld, dim, _ptr(qm),
+                                        _ptr(dm), _ptr(scores), _ptr(am), _stream()))
     return scores, am
 
 

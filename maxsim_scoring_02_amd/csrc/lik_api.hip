@@ -11,10 +11,19 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "lik.h"
 #include "lik_kernels.h"
 #include "lik_plan.h"
+
+// Fixed scratch of the allocation-free forward (lik_maxsim_fwd_noalloc):
+// every device the library runs on holds one copy, at its own address, until
+// the process ends.  In host code `scratch` only stands for the symbol; its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
 
 namespace {
 
@@ -153,6 +162,28 @@ lik_status forward_entry(int layout, const void* Q, const void* D, lik_dtype dty
 }
 
 constexpr int64_t kBwdMaxLd = 16000;   // workspace sort of grad_D: one int per row in 64 KB of LDS
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of this device's scratch (the current device's copy).
+lik_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(LIK_ERR_UNSUPPORTED, "no HIP device is available");
+  if (dev >= 64) return fail(LIK_ERR_UNSUPPORTED, "device %d: the fixed scratch serves devices 0-63", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LIK_ERR_HIP, "cannot resolve the fixed scratch on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LIK_OK;
+}
 
 lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dtype,
                           int64_t nq_or_b, int64_t Lq, int64_t nd_or_n, int64_t Ld, int64_t dim,
@@ -304,6 +335,33 @@ lik_status lik_maxsim_fwd(const void* Q, const void* D, lik_dtype dtype, int64_t
                           size_t workspace_bytes, void* stream) {
   return forward_entry(lik::kAllPairs, Q, D, dtype, Nq, Lq, Nd, Ld, dim, q_mask, d_mask, scores,
                        argmax, workspace, workspace_bytes, stream);
+}
+
+lik_status lik_maxsim_fwd_noalloc(const void* Q, const void* D, lik_dtype dtype, int64_t Nq,
+                                  int64_t Lq, int64_t Nd, int64_t Ld, int64_t dim,
+                                  const uint8_t* q_mask, const uint8_t* d_mask, float* scores,
+                                  int32_t* argmax, void* stream) {
+  Shapes s{lik::kAllPairs, Nq, Lq, Nd, Ld, dim, 0, 0, 0, 0};
+  lik_status st = check_shapes(dtype, s);
+  if (st != LIK_OK) return st;
+  if (is_zero_problem(s)) return ok();
+  const size_t need = lik::make_fwd_plan(lik::kAllPairs, (int)dtype, Nq, Lq, Nd, Ld, dim,
+                                         d_mask != nullptr, argmax != nullptr, q_mask != nullptr)
+                          .fwd_bytes;
+  if (need > kScratchBytes)
+    return fail(LIK_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch; the fixed scratch holds %zu (use "
+                "lik_maxsim_fwd with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = check_device();
+    if (st != LIK_OK) return st;
+    st = scratch_address(&ws);
+    if (st != LIK_OK) return st;
+  }
+  return forward_entry(lik::kAllPairs, Q, D, dtype, Nq, Lq, Nd, Ld, dim, q_mask, d_mask, scores,
+                       argmax, ws, need, stream);
 }
 
 lik_status lik_maxsim_bwd(const void* Q, const void* D, lik_dtype dtype, int64_t Nq, int64_t Lq,

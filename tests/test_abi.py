@@ -26,7 +26,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = _lib.header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), f"liblik.so does not export {n}"
     assert set(names) == set(_lib.SIGNATURES)
@@ -250,3 +250,20 @@ def test_plan_value_introspection(L):
     assert pv(LIK_OP_BWD, "upw") == pv(LIK_OP_FWD, "upw")
     assert pv(LIK_OP_BWD, "recompute") == 0 and pv(LIK_OP_BWD, "recompute", 2) == 1
     assert _lib.lik_plan_value(LIK_OP_FWD, (-1, 32, 4, 40, 128), LIK_BF16, 0, "upw") == -1
+
+
+def test_noalloc_forward_limits_are_checked_on_the_host(L):
+    """The allocation-free forward refuses, before any device work, a call
+    whose scratch exceeds its fixed 64 MiB, and validates arguments like the
+    workspace forward."""
+    a = (FAKE, FAKE, LIK_F16, 16, 32, 4000, 8192, 128, None, FAKE, FAKE, FAKE, None)
+    need = L.lik_workspace_bytes(LIK_OP_FWD, 16, 32, 4000, 8192, 128, LIK_F16, 3)
+    assert need > 64 << 20
+    assert L.lik_maxsim_fwd_noalloc(*a) == LIK_ERR_UNSUPPORTED
+    assert "fixed scratch" in L.lik_last_error().decode()
+    assert L.lik_maxsim_fwd_noalloc(FAKE, FAKE, 9, 2, 32, 3, 40, 128, None, None, FAKE, None,
+                                    None) == LIK_ERR_INVALID_ARG
+    assert L.lik_maxsim_fwd_noalloc(FAKE, FAKE, LIK_BF16, 0, 32, 3, 40, 128, None, None, None,
+                                    None, None) == LIK_OK
+    assert L.lik_maxsim_fwd_noalloc(FAKE, FAKE, LIK_BF16, 2, 32, 3, 40, 100, None, None, FAKE,
+                                    None, None) == LIK_ERR_UNSUPPORTED
