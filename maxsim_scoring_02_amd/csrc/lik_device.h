@@ -89,6 +89,17 @@ template <> __device__ __forceinline__ void mfma_chunk<Elem::F32>(f32x16& acc, u
   }
 }
 
+// First K-step of a tile: returns C + a*b with C = c, or 0 when ZERO, so the
+// initial value is an operand and never copied into the accumulator.
+template <Elem E, bool ZERO>
+__device__ __forceinline__ f32x16 mfma_first(u32x4 a, u32x4 b, const f32x16& c) {
+  f32x16 acc;
+  if constexpr (ZERO) acc = f32x16{};
+  else acc = c;
+  mfma_chunk<E>(acc, a, b);
+  return acc;
+}
+
 // Row of accumulator element v for a lane in half h (32x32 MFMA layout).
 __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
@@ -135,6 +146,22 @@ __device__ __forceinline__ void tile_init(f32x16& c, uint32_t word, int h) {
     const int bit = 8 * (v >> 2) + (v & 3);
     const int keep = (int)(w << (31 - bit)) >> 31;     // -1 valid, 0 masked
     c[v] = __int_as_float(~keep & (int)0xff800000u);
+  }
+}
+
+// The same for a wave-uniform word: element v of the lanes in half h comes
+// from bit 8*(v/4) + 4*h + v%4, so each element is one select under a lane
+// mask built with scalar instructions (valid rows 0, masked rows -inf).
+__device__ __forceinline__ void tile_init_uniform(f32x16& c, uint32_t word) {
+  const float ninf = -__builtin_inff();
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int b0 = 8 * (v >> 2) + (v & 3);
+    const uint64_t keep = (((word >> b0) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                          (((word >> (b0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(r) : "v"(ninf), "s"(keep));
+    c[v] = r;
   }
 }
 

@@ -237,10 +237,13 @@ constexpr int ap_lds_bytes() {
 // use them, so an MFMA waits on LDS latency only at the start of a tile.  The
 // order (kWin reads, then per chunk its MFMAs and the next read) is pinned for
 // the scheduler, which otherwise interleaves one read per MFMA pair.
-template <Elem E, int DIM, int NB>
-__device__ __forceinline__ void mfma_tile_run(f32x16 (&acc)[NB], const char* buf,
-                                              const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
-                                              int a_off) {
+// acc = C + A * B over one tile, C the tile's initial value (zero with
+// ZERO, else c0: -inf in the rows a mask removes).  The first K-step reads C
+// and writes acc, so the initial value is never copied into the accumulators.
+template <Elem E, int DIM, int NB, bool ZERO>
+__device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
+                                            const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
+                                            int a_off, const f32x16& c0) {
   using G = Geo<E, DIM>;
   constexpr int KS = G::kKSteps;
   constexpr int kWin = KS < 8 ? KS : 8;
@@ -252,33 +255,16 @@ __device__ __forceinline__ void mfma_tile_run(f32x16 (&acc)[NB], const char* buf
 #pragma unroll
   for (int m = 0; m < KS; ++m) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) mfma_chunk<E>(acc[b], av[m], bf[b][m]);
+    for (int b = 0; b < NB; ++b) {
+      if (m == 0) acc[b] = mfma_first<E, ZERO>(av[0], bf[b][0], c0);
+      else mfma_chunk<E>(acc[b], av[m], bf[b][m]);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk, 0);
     if (m + kWin < KS) {
       av[m + kWin] = ld_lds_16(buf, a_off + (m + kWin) * 32);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   }
-}
-
-template <Elem E, int DIM, int NB>
-__device__ __forceinline__ void mfma_tile_pad(f32x16 (&acc)[NB], const char* buf,
-                                              const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
-                                              int a_off) {
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
-  mfma_tile_run<E, DIM, NB>(acc, buf, bf, a_off);
-}
-
-// acc = C + A * B over one tile, with C the tile's initial value (zero, or
-// -inf in the rows a mask removes).
-template <Elem E, int DIM, int NB>
-__device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
-                                            const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
-                                            int a_off, const f32x16& c0) {
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = c0;
-  mfma_tile_run<E, DIM, NB>(acc, buf, bf, a_off);
 }
 
 // Both tiles of a super-tile at once: four independent accumulator chains
@@ -294,16 +280,6 @@ __device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB]
   constexpr int KS = G::kKSteps;
   constexpr int kWin = E == Elem::F32 ? 2 : (KS < 4 ? KS : 4);
   constexpr int kMfmaPerChunk = NB * (E == Elem::F32 ? 4 : 1);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if constexpr (ZERO) {
-      xa[b] = f32x16{};
-      xb[b] = f32x16{};
-    } else {
-      xa[b] = ca;
-      xb[b] = cb;
-    }
-  }
   u32x4 aa[KS], ab[KS];
 #pragma unroll
   for (int m = 0; m < kWin; ++m) {
@@ -314,9 +290,15 @@ __device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB]
 #pragma unroll
   for (int m = 0; m < KS; ++m) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) mfma_chunk<E>(xa[b], aa[m], bf[b][m]);
+    for (int b = 0; b < NB; ++b) {
+      if (m == 0) xa[b] = mfma_first<E, ZERO>(aa[0], bf[b][0], ca);
+      else mfma_chunk<E>(xa[b], aa[m], bf[b][m]);
+    }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) mfma_chunk<E>(xb[b], ab[m], bf[b][m]);
+    for (int b = 0; b < NB; ++b) {
+      if (m == 0) xb[b] = mfma_first<E, ZERO>(ab[0], bf[b][0], cb);
+      else mfma_chunk<E>(xb[b], ab[m], bf[b][m]);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerChunk, 0);
     if (m + kWin < KS) {
       aa[m + kWin] = ld_lds_16(bufa, a_off + (m + kWin) * 32);
@@ -599,11 +581,11 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   // never win a max), a full tile starts from zero.
   auto tile_mfma = [&](f32x16 (&X)[NB], const char* tb, uint32_t w) {
     if (w == kFull) {
-      mfma_tile_pad<E, DIM, NB>(X, tb, bf, a_off);
+      mfma_tile_c<E, DIM, NB, true>(X, tb, bf, a_off, X[0]);
     } else {
       f32x16 c0;
-      tile_init(c0, w, h);
-      mfma_tile_c<E, DIM, NB>(X, tb, bf, a_off, c0);
+      tile_init_uniform(c0, w);
+      mfma_tile_c<E, DIM, NB, false>(X, tb, bf, a_off, c0);
     }
   };
   BlockState st[NB];
@@ -648,6 +630,11 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
       for (int b = 0; b < NB; ++b) state_begin(st[b], t);
     }
     const bool step = active && has;
+    // The accumulators start each step undefined (an empty statement defines
+    // them): a value written in one step is never carried into the next, so
+    // the paths below merge without register copies.
+#pragma unroll
+    for (int b = 0; b < NB; ++b) asm volatile("" : "=v"(Xa[b]), "=v"(Xb[b]));
     if (step) {
       const char* buf = lds + cur * kSTBytes;
       if (two) {
@@ -656,12 +643,12 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
                                           Xb[0]);
         } else {
           f32x16 ca, cb;                 // a full word gives an all-zero init
-          tile_init(ca, word0, h);
-          tile_init(cb, word1, h);
+          tile_init_uniform(ca, word0);
+          tile_init_uniform(cb, word1);
           mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb);
         }
       } else {
-        tile_mfma(Xa, buf, word0);       // Xb keeps the previous step's values, unused
+        tile_mfma(Xa, buf, word0);
       }
     }
     // One fold per step on every path, so the argmax state has a single
