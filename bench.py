@@ -31,7 +31,11 @@ long-rerank, or `all` (one line each); `next` runs the long-context backward
 upstream grad, forward + backward), kd-loss-head (the kd-candidates
 inputs with the negative-doc cross-entropy as the loss head) and
 inbatch-text-f32 (the in-batch text step with float32 inputs, computed
-exactly on the fp32 MFMA and reported against its 157.3 TFLOP/s peak).
+exactly on the fp32 MFMA and reported against its 157.3 TFLOP/s peak);
+`loss-sweep` runs the loss head over batch x negatives, one line per point
+kd-loss-head-b{64,128,256}-n{2,4,8,16}: kd forward with Lq 32 and Ld 1030 in
+bf16, the negative-doc cross-entropy, and the backward, with the step's
+device memory in `config.op_bytes`.
 
 In-batch pages and kd-loss-head steps run the loss head on the GPU between
 forward and backward (cross-entropy over the score rows, library entry
@@ -191,6 +195,14 @@ class Op:
     def stream(self):
         return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
 
+    def op_bytes(self) -> int:
+        ts = [self.scores, self.argmax, self.wsf, self.wsb]
+        if self.backward:
+            ts += [self.gQ, self.gD, self.g]
+        if self.loss_head:
+            ts += [self.row_loss, self.loss, self.labels]
+        return int(sum(t.numel() * t.element_size() for t in ts if t is not None))
+
     def fwd(self):
         p, L = self.p, self.L
         Nq, Lq, Nx, Ld, dim = self.dims
@@ -291,6 +303,16 @@ def make_workload(name: str):
         w.grad = None
         w.meta["loss_head"] = "label0"
         return w, True
+    m = re.fullmatch(r"kd-loss-head-b(\d+)-n(\d+)", name)
+    if m:
+        # one point of the loss-head sweep over batch x negatives (Lq 32,
+        # Ld 1030, bf16): kd forward, negative-doc cross-entropy, backward
+        B, N = int(m.group(1)), int(m.group(2))
+        w = wl.kd_candidates(B=B, N=N)
+        w.name = name
+        w.grad = None
+        w.meta["loss_head"] = "label0"
+        return w, True
     if name == "kd-candidates":
         return wl.kd_candidates(), True
     if name == "long-docs":
@@ -314,6 +336,8 @@ def make_workload(name: str):
 
 # workloads whose line also carries the metric's memory-bound half
 SECONDARY = {"inbatch-text": "long-rerank"}
+
+LOSS_SWEEP = [f"kd-loss-head-b{b}-n{n}" for b in (64, 128, 256) for n in (2, 4, 8, 16)]
 
 DOMINANT = {  # kernel whose roofline is reported, and its bound
     "inbatch-text": ("allpairs_fwd", "mfma"),
@@ -484,7 +508,8 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
     t_fwd = float(np.mean(fwd_ms))
     t_bwd = float(np.mean(bwd_ms)) if backward else 0.0
     t_kern = float(np.mean(kern_ms))
-    kern, bound = DOMINANT[name]
+    kern, bound = DOMINANT.get(name, ("pairs_fwd", "hbm") if name.startswith("kd-loss-head-b")
+                               else (None, None))
     if bound == "mfma":
         flops = f_fwd + (f_bwd if backward else 0.0)
         value = flops / (ms_step * 1e-3) / 1e12
@@ -526,6 +551,10 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
             "fwd_bytes": b_fwd,
             "bwd_bytes": b_bwd,
             "wall_s_timed": round(wall, 4),
+            # device memory the operator holds for one step: outputs, argmax,
+            # float32 gradients, loss-head buffers and workspaces (the
+            # library allocates nothing itself)
+            "op_bytes": op.op_bytes(),
         },
         "roofline": {
             "bound": bound,
@@ -601,7 +630,8 @@ def main():
         copy_calibration(args.copy_calibration, max(args.steps, 1))
         return
     groups = {"all": ["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"],
-              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head", "inbatch-text-f32"]}
+              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head", "inbatch-text-f32"],
+              "loss-sweep": LOSS_SWEEP}
     names = groups.get(args.workload, [args.workload])
     for i, name in enumerate(names):
         line = bench_one(name, args.steps, args.warmup,

@@ -841,23 +841,30 @@ __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // combine: one wave per output (query, doc) / pair
 // ---------------------------------------------------------------------------
-// One workgroup per output: 64 query-token lanes x 4 chunk groups; each
-// thread merges every 4th chunk with independent loads, then group 0 merges
-// the 4 partials (the larger max wins, ties to the lower index: the result
-// does not depend on the merge order) and sums over the valid tokens.
+// Many chunks: one workgroup per output.  Its 256 threads are TG query-token
+// lanes (32, or 64 when Lq > 32) x G = 256 / TG chunk groups; a thread merges
+// the chunks c = g, g + G, ... with all of its loads issued before any is
+// used (up to 16 at a time), then group 0 merges the G group results in
+// group order and sums over the valid tokens.  Merge rule: the larger max
+// wins, ties to the lower index, so the result does not depend on the order
+// in which chunks are merged.
 __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
-  __shared__ float sM[4][64];
-  __shared__ int sJ[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 6;
+  __shared__ float sM[8][64];
+  __shared__ int sJ[8][64];
+  const int tid = threadIdx.x;
+  const int TG = a.Lq <= 32 ? 32 : 64;       // token lanes per group
+  const int G = 256 / TG;                     // chunk groups
+  const int tl = tid % TG, grp = tid / TG;
   const bool ap = a.layout == kAllPairs;
   const int64_t n_out = ap ? a.Nq * a.n_docs : a.n_docs;
+  const int64_t stride = a.n_docs * a.n_cg * a.SPW;      // between chunks
   for (int64_t out = blockIdx.x; out < n_out; out += gridDim.x) {
     const int64_t q = ap ? out / a.n_docs : out / a.K;
     const int64_t e = ap ? out - q * a.n_docs : out;
     const bool empty = a.ntiles ? a.ntiles[e] == 0 : a.Ld == 0;
     float total = 0.0f;
-    for (int64_t i0 = 0; i0 < a.Lq; i0 += 64) {
-      const int64_t i = i0 + lane;
+    for (int64_t i0 = 0; i0 < a.Lq; i0 += TG) {
+      const int64_t i = i0 + tl;
       const bool ok = i < a.Lq;
       int64_t cg, slot;
       bool have = ok;                        // this token has partials
@@ -882,15 +889,14 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
       float M = -__builtin_inff();
       int J = -1;
       if (have) {
-        const int64_t stride = a.n_docs * a.n_cg * a.SPW;      // between chunks
         const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
-        constexpr int U = 4;
-        for (int64_t c0 = grp; c0 < a.nchunks; c0 += 4 * U) {
+        constexpr int U = 16;
+        for (int64_t c0 = grp; c0 < a.nchunks; c0 += (int64_t)G * U) {
           float mm[U];
           int jj[U];
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const int64_t c = c0 + 4 * u;
+            const int64_t c = c0 + (int64_t)G * u;
             mm[u] = -__builtin_inff();
             jj[u] = -1;
             if (c < a.nchunks) {
@@ -903,14 +909,15 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
           for (int u = 0; u < U; ++u) merge_mj(M, J, mm[u], jj[u]);
         }
       }
-      sM[grp][lane] = M;
-      sJ[grp][lane] = J;
+      sM[grp][tl] = M;
+      sJ[grp][tl] = J;
       __syncthreads();
       if (grp == 0) {
-#pragma unroll
-        for (int g2 = 1; g2 < 4; ++g2) merge_mj(M, J, sM[g2][lane], sJ[g2][lane]);
+        for (int g2 = 1; g2 < G; ++g2) merge_mj(M, J, sM[g2][tl], sJ[g2][tl]);
         const bool tok = ok && (!a.q_mask || a.q_mask[q * a.Lq + i]);
-        total += wave_sum(tok ? M : 0.0f);
+        float v = tok ? M : 0.0f;
+        for (int k = TG >> 1; k >= 1; k >>= 1) v += __shfl_xor(v, k, TG);
+        total += v;
         if (ok && a.argmax) a.argmax[out * a.Lq + i] = (tok && !empty) ? J : -1;
       }
       __syncthreads();
