@@ -148,7 +148,8 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq,
  *            "gd_mode" (grad_D kernel: 0 workspace sort, 1 sorted in LDS
  *            per all-pairs document, 2 pairwise/kd streaming), "gd_parts",
  *            "gs_split", "gs_sw", "gs_lds", "gq_ap" (all-pairs grad_Q by
- *            document rounds), "gq_slices", "recompute";
+ *            document rounds), "gq_slices", "recompute", "sort_batch"
+ *            (workspace sort: documents per batch, 0 when not used);
  *   both     "workspace" (the same as lik_workspace_bytes).
  * Returns -1 for an unknown key, a key of the other direction, or sizes
  * lik_workspace_bytes rejects.  Host only; no device is touched.

@@ -323,7 +323,8 @@ int64_t lik_plan_value(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or_n, 
   struct KV { const char* k; int64_t v; };
   const KV kv[] = {{"gd_mode", b.gd_mode},     {"gd_parts", b.gd_parts}, {"gs_split", b.gs_split},
                    {"gs_sw", b.gs_sw},         {"gq_ap", b.gq_ap},       {"gq_slices", b.gq_slices},
-                   {"recompute", b.recompute}, {"gs_lds", (int64_t)b.gs_lds}};
+                   {"recompute", b.recompute}, {"gs_lds", (int64_t)b.gs_lds},
+                   {"sort_batch", b.sort_batch}};
   for (const KV& e : kv)
     if (std::strcmp(key, e.k) == 0) return e.v;
   return fwd_plan_value(b.fwd, key);

@@ -63,6 +63,7 @@ struct BwdArgs {
       gs_off_part;                          // LDS layout
   uint64_t lq_magic;                        // ceil(2^32 / Lq): h / Lq for h < 2^16
   int64_t Nq, Lq, n_docs, Ld, K, H;
+  int64_t e0, nb;                           // workspace sort: first document and documents of a batch
 };
 
 // ---------------------------------------------------------------------------
@@ -298,7 +299,8 @@ __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
   int* cur = smem;             // counts, then (in place) the running row cursors
   int* wtot = smem + Ld;       // 4 wave totals
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t e = blockIdx.x;
+  const int64_t el = blockIdx.x;          // document of the batch (workspace index)
+  const int64_t e = a.e0 + el;            // document
   const int64_t H = a.H;
 
   for (int j = tid; j < Ld; j += 256) cur[j] = 0;
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
   __syncthreads();
   int base = incl - local;
   for (int w = 0; w < wave; ++w) base += wtot[w];
-  int32_t* roff = a.roff + e * (a.Ld + 1);
+  int32_t* roff = a.roff + el * (a.Ld + 1);
   for (int j = lo; j < hi; ++j) {
     const int c = cur[j];
     cur[j] = base;
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
   __syncthreads();
 
   // stable placement: waves take turns over each group of 256 hits
-  int32_t* out = a.sorted + e * H;
+  int32_t* out = a.sorted + el * H;
   const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   for (int64_t h0 = 0; h0 < H; h0 += 256) {
     for (int w = 0; w < 4; ++w) {
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
           int64_t qrow, p;
           hit_qrow_pair(a, e, h, qrow, p);
           out[pos + rank] = (int32_t)qrow;
-          a.sorted_g[e * H + pos + rank] = a.g[p];
+          a.sorted_g[el * H + pos + rank] = a.g[p];
         }
         if (v && rank == count - 1) cur[j] = pos + count;
       }
@@ -379,7 +381,8 @@ __global__ __launch_bounds__(256) void gradd_sort_waves_kernel(BwdArgs a) {
   int* cnt = smem;               // [4][Ld] counts, then running cursors
   int* wtot = smem + 4 * Ld;     // 4 wave totals of the scan
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t e = blockIdx.x;
+  const int64_t el = blockIdx.x;          // document of the batch (workspace index)
+  const int64_t e = a.e0 + el;            // document
   const int64_t H = a.H;
   const int64_t Hq = ((H + 255) / 256) * 64;   // hits per wave, a multiple of 64
   const int64_t h0 = min(wave * Hq, H), h1 = min(h0 + Hq, H);
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(256) void gradd_sort_waves_kernel(BwdArgs a) {
   __syncthreads();
   int base = incl - local;
   for (int w = 0; w < wave; ++w) base += wtot[w];
-  int32_t* roff = a.roff + e * (a.Ld + 1);
+  int32_t* roff = a.roff + el * (a.Ld + 1);
   for (int j = lo; j < hi; ++j) {
     roff[j] = base;
 #pragma unroll
@@ -430,8 +433,8 @@ __global__ __launch_bounds__(256) void gradd_sort_waves_kernel(BwdArgs a) {
   if (tid == 0) roff[Ld] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
   __syncthreads();
 
-  int32_t* out = a.sorted + e * H;
-  float* outg = a.sorted_g + e * H;
+  int32_t* out = a.sorted + el * H;
+  float* outg = a.sorted_g + el * H;
   const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   // rows of the next chunk of 64 hits are loaded while this chunk is placed
   int jn = (h0 + lane < h1) ? hit_row(a, e, h0 + lane) : -1;
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(256) void gradd_rows_group_kernel(BwdArgs a, int rp
   const int tid = threadIdx.x;
   const int c = tid % CPR;
   const int64_t gid = (int64_t)blockIdx.x * GPB + tid / CPR;
-  const int64_t n_rows = a.n_docs * a.Ld;
+  const int64_t n_rows = a.nb * a.Ld;      // rows of the batch's documents
   const int64_t row0 = gid * rpg;
   if (row0 >= n_rows) return;
   const char* Qb = (const char*)a.Q;
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(256) void gradd_rows_group_kernel(BwdArgs a, int rp
         for (int k = 0; k < EPC; ++k) acc[k] = __builtin_fmaf(gg[m], f[k], acc[k]);
       }
     }
-    float* out = a.gD + row * DIM + c * EPC;
+    float* out = a.gD + (a.e0 * a.Ld + row) * DIM + c * EPC;
 #pragma unroll
     for (int k = 0; k < EPC; k += 4)
       *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
@@ -979,7 +982,7 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
       const int row = r0 + u * RPI + sub;
       if (sub < RPI && row < r_end) {
         const f32x4 w = {v[u][0], v[u][1], v[u][2], v[u][3]};
-        __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f));
+        *reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f) = w;
       }
     }
   }
@@ -1041,25 +1044,33 @@ static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t gs_lds, hipStr
                        dim3((unsigned)cdiv(a.n_docs * a.gd_parts, 4)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (a.Ld <= kSortWavesMaxLd) {
-    const size_t lds = (size_t)(4 * a.Ld + 4) * sizeof(int);
-    hipLaunchKernelGGL(gradd_sort_waves_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
-  } else {
-    const size_t lds = (size_t)(a.Ld + 4) * sizeof(int);
-    hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)a.n_docs), dim3(256), lds, s, a);
+  // documents are sorted and summed in batches that fit the workspace
+  for (int64_t e0 = 0; e0 < a.n_docs; e0 += a.nb) {
+    BwdArgs b = a;
+    b.e0 = e0;
+    b.nb = a.n_docs - e0 < a.nb ? a.n_docs - e0 : a.nb;
+    if (b.Ld <= kSortWavesMaxLd) {
+      const size_t lds = (size_t)(4 * b.Ld + 4) * sizeof(int);
+      hipLaunchKernelGGL(gradd_sort_waves_kernel, dim3((unsigned)b.nb), dim3(256), lds, s, b);
+    } else {
+      const size_t lds = (size_t)(b.Ld + 4) * sizeof(int);
+      hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)b.nb), dim3(256), lds, s, b);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // rows per group: one while groups are scarce; up to 16 (one offsets
+    // load) when the output is large and mostly empty rows
+    const int64_t n_rows = b.nb * b.Ld;
+    int rpg = (int)cdiv(n_rows, 256 * 256);
+    const int max_rpg = CPR < 16 ? CPR : 16;
+    rpg = rpg < 1 ? 1 : (rpg > max_rpg ? max_rpg : rpg);
+    const int64_t gpb = 256 / CPR;
+    hipLaunchKernelGGL((gradd_rows_group_kernel<E, DIM>),
+                       dim3((unsigned)cdiv(cdiv(n_rows, rpg), gpb)), dim3(256), 0, s, b, rpg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // rows per group: one while groups are scarce; up to 16 (one offsets
-  // load) when the output is large and mostly empty rows
-  const int64_t n_rows = a.n_docs * a.Ld;
-  int rpg = (int)cdiv(n_rows, 256 * 256);
-  const int max_rpg = CPR < 16 ? CPR : 16;
-  rpg = rpg < 1 ? 1 : (rpg > max_rpg ? max_rpg : rpg);
-  const int64_t gpb = 256 / CPR;
-  hipLaunchKernelGGL((gradd_rows_group_kernel<E, DIM>),
-                     dim3((unsigned)cdiv(cdiv(n_rows, rpg), gpb)), dim3(256), 0, s, a, rpg);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <Elem E, int DIM>
@@ -1137,6 +1148,8 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
   a.Ld = f.Ld;
   a.K = f.K;
   a.H = p.H;
+  a.e0 = 0;
+  a.nb = p.sort_batch;
   const bool wq = grad_Q != nullptr, wd = grad_D != nullptr;
   switch (f.elem) {
     case 0: return grads_dim<Elem::F16>(p, a, wq, wd, s);

@@ -55,6 +55,7 @@ enum GdMode : int {
 constexpr int kGdPairsMinParts = 4;
 constexpr int64_t kGdPairsWaves = 65536;
 constexpr int64_t kGdPairsMinRows = 64;   // rows a wave streams, at least
+constexpr size_t kSortWsMax = size_t(256) << 20;  // workspace-sort batches stay within this
 constexpr int kGsThreads = 1024;       // threads of the sorted grad_D workgroup
 constexpr int kGsLdsMax = 160 * 1024;  // LDS of one CU
 constexpr int kPairsMaxLq = 256;   // longest query of the pairs grad_D kernel
@@ -76,6 +77,7 @@ struct BwdPlan {
   int gs_off_sorted = 0, gs_off_start = 0, gs_off_gl = 0, gs_off_keys = 0, gs_off_hist = 0,
       gs_off_masks = 0, gs_off_part = 0;
   size_t gs_lds = 0;
+  int64_t sort_batch = 0;   // workspace sort: documents sorted per batch (bounded workspace)
   bool gq_ap = false;       // all-pairs grad_Q by document rounds (gradq_ap_kernel)
   int gq_slices = 1;        // >1: grad_Q gathered per document slice, then reduced
   size_t off_argmax = 0, off_scores = 0, off_sorted = 0, off_sorted_g = 0, off_roff = 0, off_fwd = 0,
@@ -319,12 +321,20 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
     off = align256(off + f.fwd_bytes);
   }
   if (Lq > 0 && Ld > 0 && b.gd_mode == kGdSort) {
+    // sorted hit lists and row offsets for at most sort_batch documents at a
+    // time, so that the workspace stays within kSortWsMax (one document may
+    // exceed it on its own)
+    const size_t per_doc = (size_t)b.H * 8 + (size_t)(Ld + 1) * 4;
+    int64_t nbat = (int64_t)(kSortWsMax / per_doc);
+    if (nbat < 1) nbat = 1;
+    if (nbat > f.n_docs) nbat = f.n_docs;
+    b.sort_batch = nbat;
     b.off_sorted = off;
-    off = align256(off + (size_t)f.n_docs * b.H * 4);
+    off = align256(off + (size_t)nbat * b.H * 4);
     b.off_sorted_g = off;
-    off = align256(off + (size_t)f.n_docs * b.H * 4);
+    off = align256(off + (size_t)nbat * b.H * 4);
     b.off_roff = off;
-    off = align256(off + (size_t)f.n_docs * (Ld + 1) * 4);
+    off = align256(off + (size_t)nbat * (Ld + 1) * 4);
   }
   if (b.gq_slices > 1) {
     b.off_gq_part = off;

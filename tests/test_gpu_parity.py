@@ -211,6 +211,50 @@ def test_many_documents_grad_q_per_xcd_slice():
     full_check(_custom("many-docs", "allpairs", "bf16", Q, D, qm, dm, g))
 
 
+def test_workspace_sort_in_document_batches():
+    """More than 65535 hits per document (2100 queries x 32 tokens) puts
+    grad_D on the workspace sort, whose workspace holds a bounded batch of
+    documents: 600 documents run as two batches.  The GPU runs the whole
+    problem; sampled documents at the batch edges are compared with the
+    oracle, with the upstream grad zeroed outside them (so grad_Q sums the
+    sampled documents only) and every other document's grad_D exactly zero."""
+    from maxsim_scoring_02_amd import _lib
+
+    rng = np.random.default_rng(1600)
+    Nq, Lq, Nd, Ld, dim = 2100, 32, 600, 64, 128
+    pv = lambda k: _lib.lik_plan_value(_lib.LIK_OP_BWD, (Nq, Lq, Nd, Ld, dim), _lib.LIK_BF16, 1 | 2,
+                                       k)
+    nb = pv("sort_batch")
+    assert pv("gd_mode") == 0 and 1 <= nb < Nd, (pv("gd_mode"), nb)
+    say(f"[plan] workspace sort: {nb} documents per batch, "
+        f"workspace {pv('workspace') / 2**20:.1f} MiB")
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    D = _rand_tokens(rng, (Nd, Ld, dim))
+    dm = np.arange(Ld)[None] < rng.integers(1, Ld + 1, Nd)[:, None]
+    dm[5] = False                                    # an empty document
+    docs = sorted({0, 5, nb - 1, nb, Nd - 1})
+    g = rng.standard_normal((Nq, Nd)).astype(np.float32)
+    keep = np.zeros(Nd, bool)
+    keep[docs] = True
+    g[:, ~keep] = 0.0
+    w = _custom("sort-batches", "allpairs", "bf16", Q, D, None, dm, g)
+    dev = torch.device("cuda:0")
+    Qd, Dd, dmd = w.Q.to(dev), w.D.to(dev), w.d_mask.to(dev)
+    s, a = _lib.lik_maxsim_fwd(Qd, Dd, None, dmd)
+    gQ, gD = _lib.lik_maxsim_bwd(Qd, Dd, torch.from_numpy(g).to(dev), a, None, dmd)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(gD)) == int(torch.count_nonzero(gD[docs]))
+    sub = Workload("sort-batches-docs", "allpairs", "bf16", w.Q, w.D[docs].contiguous(), None,
+                   w.d_mask[docs].contiguous(), None)
+    Qn, Dn, _, dmn = sub.numpy_inputs()
+    ref = oracle.maxsim_allpairs(Qn, Dn, None, dmn)
+    check_scores(s[:, docs].cpu().numpy(), ref)
+    merged = check_argmax(a[:, docs].cpu().numpy(), ref, sub)
+    rQ, rD = oracle.maxsim_allpairs_bwd(Qn, Dn, g[:, docs].astype(np.float64), merged, None, dmn)
+    check_grads(gQ.cpu().numpy(), rQ, "grad_Q")
+    check_grads(gD[docs].cpu().numpy(), rD, "grad_D")
+
+
 def test_hub_rows_collect_most_hits():
     """A few document rows are the argmax of almost every query token, so a
     row's sorted hits span many lane groups and its gradient row is put

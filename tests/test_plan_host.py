@@ -15,6 +15,8 @@ checking it themselves:
   slots for every token, token tables inside the workspace;
 - fused grad_D: its LDS layout fits the size the plan reports and each
   sorting wave ranks at most the hits it can hold;
+- workspace-sort grad_D: documents in the largest batches whose sorted
+  lists stay within the workspace cap, regions inside the workspace;
 - pairwise / kd grad_D: waves per document at least the minimum, split
   finer only when the batch is too small to fill the chip, never below the
   minimum rows per wave, and the grid fits.
@@ -130,6 +132,20 @@ static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     CHECK(b.gs_lds <= (size_t)kGsLdsMax, "LDS %zu", b.gs_lds);
     CHECK(b.gs_off_hist % 16 == 0 && b.gs_off_part % 16 == 0, "alignment");
   }
+  if (b.gd_mode == kGdSort && Lq > 0 && Ld > 0) {
+    // workspace sort: documents in batches whose sorted lists and row
+    // offsets stay within kSortWsMax (one document may exceed it), the
+    // largest such batch, and the regions inside the workspace
+    const size_t per_doc = (size_t)b.H * 8 + (size_t)(Ld + 1) * 4;
+    const size_t ws = (size_t)b.sort_batch * per_doc;
+    CHECK(b.sort_batch >= 1 && b.sort_batch <= b.fwd.n_docs, "sort batch %ld", (long)b.sort_batch);
+    CHECK(b.sort_batch == 1 || ws <= kSortWsMax, "sort workspace %zu", ws);
+    CHECK(b.sort_batch == b.fwd.n_docs || ws + per_doc > kSortWsMax, "sort batch not maximal");
+    CHECK(b.off_sorted_g >= b.off_sorted + (size_t)b.sort_batch * b.H * 4 &&
+              b.off_roff >= b.off_sorted_g + (size_t)b.sort_batch * b.H * 4 &&
+              b.off_roff + (size_t)b.sort_batch * (Ld + 1) * 4 <= b.total,
+          "sort regions");
+  }
   if (b.gq_ap) {
     const long esize = elem == 2 ? 4 : 2;
     CHECK(layout == kAllPairs && b.gq_slices >= 1, "grad_Q rounds");
@@ -171,6 +187,15 @@ int main() {
               bwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim);
               bwd_case(kKd, elem, Nq, Lq, Nd % 32 + 1, Ld, dim);
             }
+  // hit lists past the sorted kernel's 16-bit hit numbers: the workspace sort
+  // in one batch, several batches, and one document per batch
+  for (int elem = 0; elem < 3; ++elem) {
+    bwd_case(kAllPairs, elem, 2100, 32, 150, 64, 128);
+    bwd_case(kAllPairs, elem, 2100, 32, 600, 64, 128);
+    bwd_case(kAllPairs, elem, 20000, 32, 1000, 300, 128);
+    bwd_case(kAllPairs, elem, 4, 32, 3, 40000, 128);
+    bwd_case(kPairwise, elem, 64, 100, 1, 32768, 128);
+  }
   std::printf("fails %d\n", fails);
   return fails ? 1 : 0;
 }
