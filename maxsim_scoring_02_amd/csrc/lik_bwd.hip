@@ -15,7 +15,9 @@
 //                          (row offset, weight) that the others read by a lane
 //                          broadcast; with several document slices (workgroup
 //                          b runs on XCD b % 8 and takes slice b % slices)
-//                          gradq_reduce_kernel adds the partials in slice order
+//                          the partials are added in slice order at the start
+//                          of the sorted grad_D kernel that follows, or by
+//                          gradq_reduce_kernel when that kernel does not run
 //     gradq_kernel         few documents per query (pairwise, kd, small Nd)
 //   grad_D
 //     gradd_sorted_kernel  all-pairs: per document, one workgroup sorts its
@@ -64,6 +66,7 @@ struct BwdArgs {
   uint64_t lq_magic;                        // ceil(2^32 / Lq): h / Lq for h < 2^16
   int64_t Nq, Lq, n_docs, Ld, K, H;
   int64_t e0, nb;                           // workspace sort: first document and documents of a batch
+  int gq_red;                               // the sorted grad_D kernel also adds the grad_Q partials
 };
 
 // ---------------------------------------------------------------------------
@@ -248,11 +251,10 @@ __global__ __launch_bounds__(256) void gradq_ap_kernel(BwdArgs a) {
     *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
 }
 
-// grad_Q = sum of the slice partials, added in slice order.
-__global__ __launch_bounds__(256) void gradq_reduce_kernel(const float4* __restrict__ part, int ns,
-                                                           int64_t n4, float4* __restrict__ gQ) {
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k >= n4) return;
+// grad_Q element group k (four floats) = sum of the slice partials, added in
+// slice order.
+__device__ __forceinline__ void gradq_reduce_at(const float4* __restrict__ part, int ns, int64_t n4,
+                                                float4* __restrict__ gQ, int64_t k) {
   float4 s = part[k];
   for (int x = 1; x < ns; ++x) {
     const float4 v = part[(int64_t)x * n4 + k];
@@ -262,6 +264,12 @@ __global__ __launch_bounds__(256) void gradq_reduce_kernel(const float4* __restr
     s.w += v.w;
   }
   gQ[k] = s;
+}
+
+__global__ __launch_bounds__(256) void gradq_reduce_kernel(const float4* __restrict__ part, int ns,
+                                                           int64_t n4, float4* __restrict__ gQ) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k < n4) gradq_reduce_at(part, ns, n4, gQ, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -624,6 +632,17 @@ __global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
   const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   const bool use_masks = a.gs_masks != 0;
   float* __restrict__ gD_doc = a.gD + e * (int64_t)Ld * DIM;
+
+  // The grad_Q slice partials (written by the previous launch on this
+  // stream) are added here, spread over the grid, instead of in a kernel of
+  // their own.
+  if (a.gq_red) {
+    const int64_t n4 = a.Nq * a.Lq * (DIM / 4);
+    for (int64_t k = (int64_t)blockIdx.x * kGsThreads + tid; k < n4;
+         k += (int64_t)gridDim.x * kGsThreads)
+      gradq_reduce_at(reinterpret_cast<const float4*>(a.gq_part), a.gq_slices, n4,
+                      reinterpret_cast<float4*>(a.gQ), k);
+  }
 
   // 0. clear the histograms and match words; this document's upstream grads
   for (int k = tid; k < SW * Ld; k += kGsThreads) {
@@ -1012,7 +1031,7 @@ static hipError_t launch_gradq(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gradq_ap_kernel<E, DIM>), dim3((unsigned)(a.gq_slices * cdiv(n_tok, TPB))),
                        dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.gq_slices == 1) return e;
+    if (e != hipSuccess || a.gq_slices == 1 || a.gq_red) return e;
     const int64_t n4 = n_tok * DIM / 4;
     hipLaunchKernelGGL(gradq_reduce_kernel, dim3((unsigned)cdiv(n4, 256)), dim3(256), 0, s,
                        reinterpret_cast<const float4*>(a.gq_part), a.gq_slices, n4,
@@ -1151,6 +1170,9 @@ hipError_t run_backward(const BwdPlan& p, const void* Q, const void* D, const ui
   a.e0 = 0;
   a.nb = p.sort_batch;
   const bool wq = grad_Q != nullptr, wd = grad_D != nullptr;
+  // with both gradients, the sorted grad_D kernel (launched after grad_Q on
+  // the same stream) adds the grad_Q slice partials
+  a.gq_red = (wq && wd && p.gq_ap && p.gq_slices > 1 && p.gd_mode == kGdSorted) ? 1 : 0;
   switch (f.elem) {
     case 0: return grads_dim<Elem::F16>(p, a, wq, wd, s);
     case 1: return grads_dim<Elem::BF16>(p, a, wq, wd, s);

@@ -211,6 +211,37 @@ def test_many_documents_grad_q_per_xcd_slice():
     full_check(_custom("many-docs", "allpairs", "bf16", Q, D, qm, dm, g))
 
 
+def test_grad_q_alone_and_grad_d_alone_match_the_joint_call():
+    """With both gradients the grad_D kernel also adds the grad_Q slice
+    partials; asked for one gradient only, the partials go through their own
+    kernel.  Both routes add the same partials in the same order: grad_Q and
+    grad_D are bitwise equal either way (and the joint call is checked
+    against the oracle)."""
+    from maxsim_scoring_02_amd import _lib
+
+    rng = np.random.default_rng(1301)
+    Nq, Nd, Lq, Ld, dim = 12, 80, 32, 70, 128
+    pv = lambda k: _lib.lik_plan_value(_lib.LIK_OP_BWD, (Nq, Lq, Nd, Ld, dim), _lib.LIK_BF16,
+                                       1 | 2, k)
+    assert pv("gq_ap") == 1 and pv("gq_slices") > 1 and pv("gd_mode") == 1
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    D = _rand_tokens(rng, (Nd, Ld, dim))
+    dm = np.arange(Ld)[None] < rng.integers(1, Ld + 1, Nd)[:, None]
+    g = rng.standard_normal((Nq, Nd))
+    w = _custom("grad-routes", "allpairs", "bf16", Q, D, None, dm, g)
+    full_check(w)
+    dev = torch.device("cuda:0")
+    Qd, Dd, dmd = w.Q.to(dev), w.D.to(dev), w.d_mask.to(dev)
+    gd = w.grad.to(dev)
+    _, a = _lib.lik_maxsim_fwd(Qd, Dd, None, dmd)
+    gQ, gD = _lib.lik_maxsim_bwd(Qd, Dd, gd, a, None, dmd)
+    gQ1, none_d = _lib.lik_maxsim_bwd(Qd, Dd, gd, a, None, dmd, need_grad_d=False)
+    none_q, gD1 = _lib.lik_maxsim_bwd(Qd, Dd, gd, a, None, dmd, need_grad_q=False)
+    torch.cuda.synchronize()
+    assert none_d is None and none_q is None
+    assert torch.equal(gQ, gQ1) and torch.equal(gD, gD1)
+
+
 def test_workspace_sort_in_document_batches():
     """More than 65535 hits per document (2100 queries x 32 tokens) puts
     grad_D on the workspace sort, whose workspace holds a bounded batch of
