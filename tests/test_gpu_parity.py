@@ -242,6 +242,44 @@ def test_grad_q_alone_and_grad_d_alone_match_the_joint_call():
     assert torch.equal(gQ, gQ1) and torch.equal(gD, gD1)
 
 
+def test_mask_bytes_of_any_nonzero_value_on_both_mask_paths():
+    """Mask bytes of any nonzero value count as valid.  Mask rows of whole
+    dwords at a 4-byte aligned address are turned into tile words four bytes
+    per lane; the same mask at an odd address one byte per lane: scores and
+    argmax must be bitwise equal, and both match the oracle."""
+    from maxsim_scoring_02_amd import _lib
+
+    rng = np.random.default_rng(1302)
+    Nq, Lq, Nd, Ld, dim = 6, 32, 9, 100, 128
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    D = _rand_tokens(rng, (Nd, Ld, dim))
+    vals = np.array([1, 2, 0x7F, 0x80, 0xFF], dtype=np.uint8)
+    u = np.where(rng.random((Nd, Ld)) < 0.7, rng.choice(vals, (Nd, Ld)), 0).astype(np.uint8)
+    u[1, 32:64] = 0                                   # a masked middle tile
+    u[2] = 0                                          # an empty document
+    u[3] = 0
+    u[3, Ld - 1] = 0x80                               # only the last row
+    u[4, :] = 0xFF                                    # every row
+    dev = torch.device("cuda:0")
+    w = _custom("byte-mask", "allpairs", "bf16", Q, D, None, u != 0, None)
+    Qd, Dd = w.Q.to(dev), w.D.to(dev)
+    aligned = torch.from_numpy(u).to(dev).view(torch.bool)
+    assert aligned.data_ptr() % 4 == 0 and Ld % 4 == 0
+    buf = torch.zeros(Nd * Ld + 1, dtype=torch.uint8, device=dev)
+    buf[1:] = torch.from_numpy(u.reshape(-1)).to(dev)
+    odd = buf[1:].view(Nd, Ld).view(torch.bool)
+    assert odd.data_ptr() % 4 != 0
+    s1, a1 = _lib.lik_maxsim_fwd(Qd, Dd, None, aligned)
+    s2, a2 = _lib.lik_maxsim_fwd(Qd, Dd, None, odd)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(a1, a2)
+    Qn, Dn, _, dmn = w.numpy_inputs()
+    ref = oracle.maxsim_allpairs(Qn, Dn, None, dmn)
+    check_scores(s1.cpu().numpy(), ref)
+    check_argmax(a1.cpu().numpy(), ref, w)
+    assert float(s1[0, 2]) == -1e9
+
+
 def test_workspace_sort_in_document_batches():
     """More than 65535 hits per document (2100 queries x 32 tokens) puts
     grad_D on the workspace sort, whose workspace holds a bounded batch of
