@@ -46,9 +46,9 @@
  *                         size, unknown dtype, misaligned pointer, workspace
  *                         too small;
  *   LIK_ERR_UNSUPPORTED   a valid request the library does not implement
- *                         (see lik_supported_dim; backward with Ld >
- *                         16000; all-pairs with Nd >= 2^23, Ld >
- *                         261120 or Nq * Lq > 2^30; no gfx950 device);
+ *                         (see lik_supported_dim; all-pairs with
+ *                         Nd >= 2^23, Ld > 261120 or Nq * Lq > 2^30; no
+ *                         gfx950 device);
  *   LIK_ERR_HIP           a HIP launch error, reported as it happens.
  *   Zero-sized batches (Nq, Nd, B or N of 0) are a successful no-op.
  * Determinism.  For identical inputs and shapes the results are bitwise

@@ -161,8 +161,6 @@ lik_status forward_entry(int layout, const void* Q, const void* D, lik_dtype dty
   return ok();
 }
 
-constexpr int64_t kBwdMaxLd = 16000;   // workspace sort of grad_D: one int per row in 64 KB of LDS
-
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[64] = {};
 
@@ -206,13 +204,6 @@ lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dt
   if (st != LIK_OK) return st;
   lik::BwdPlan p = lik::make_bwd_plan(layout, (int)dtype, nq_or_b, Lq, nd_or_n, Ld, dim,
                                       d_mask != nullptr, argmax != nullptr, q_mask != nullptr);
-  // only the workspace sort of grad_D keeps per-row tables in LDS; the fused
-  // all-pairs kernel sizes its own LDS and the pairwise/kd kernel streams rows
-  if (grad_D && p.gd_mode == lik::kGdSort && Ld > kBwdMaxLd)
-    return fail(LIK_ERR_UNSUPPORTED,
-                "backward with this shape sorts grad_D through the workspace, which supports "
-                "Ld <= %lld (got %lld)",
-                (long long)kBwdMaxLd, (long long)Ld);
   if (ws_bytes < p.total)
     return fail(LIK_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", ws_bytes,
                 p.total);

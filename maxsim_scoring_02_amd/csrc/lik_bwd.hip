@@ -301,79 +301,92 @@ __device__ __forceinline__ void hit_qrow_pair(const BwdArgs& a, int64_t e, int64
   }
 }
 
+// Rows are taken in windows of at most kSortWin (one int of LDS per row), so
+// documents of any length sort in 64 KB of LDS: per window, the hits on its
+// rows are counted, their row starts follow the hits of earlier windows, and
+// they are placed in hit order.  Every window reads the hits' rows again.
+constexpr int kSortWin = 16000;
+
 __global__ __launch_bounds__(256) void gradd_sort_kernel(BwdArgs a) {
   extern __shared__ int smem[];
   const int Ld = (int)a.Ld;
-  int* cur = smem;             // counts, then (in place) the running row cursors
-  int* wtot = smem + Ld;       // 4 wave totals
+  const int W = Ld < kSortWin ? Ld : kSortWin;
+  int* cur = smem;             // counts, then (in place) the running row cursors of a window
+  int* wtot = smem + W;        // 4 wave totals
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t el = blockIdx.x;          // document of the batch (workspace index)
   const int64_t e = a.e0 + el;            // document
   const int64_t H = a.H;
-
-  for (int j = tid; j < Ld; j += 256) cur[j] = 0;
-  __syncthreads();
-  for (int64_t h = tid; h < H; h += 256) {
-    const int j = hit_row(a, e, h);
-    if (j >= 0) atomicAdd(&cur[j], 1);
-  }
-  __syncthreads();
-
-  // exclusive scan of the counts, in place; each thread owns a segment
-  const int seg = (Ld + 255) / 256;
-  const int lo = min(tid * seg, Ld), hi = min(lo + seg, Ld);
-  int local = 0;
-  for (int j = lo; j < hi; ++j) local += cur[j];
-  int incl = local;
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) {
-    const int t = __shfl_up(incl, k);
-    if (lane >= k) incl += t;
-  }
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  int base = incl - local;
-  for (int w = 0; w < wave; ++w) base += wtot[w];
   int32_t* roff = a.roff + el * (a.Ld + 1);
-  for (int j = lo; j < hi; ++j) {
-    const int c = cur[j];
-    cur[j] = base;
-    roff[j] = base;
-    base += c;
-  }
-  if (tid == 0) roff[Ld] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-  __syncthreads();
-
-  // stable placement: waves take turns over each group of 256 hits
   int32_t* out = a.sorted + el * H;
   const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int64_t h0 = 0; h0 < H; h0 += 256) {
-    for (int w = 0; w < 4; ++w) {
-      if (wave == w) {
-        const int64_t h = h0 + w * 64 + lane;
-        const int j = h < H ? hit_row(a, e, h) : -1;
-        const bool v = j >= 0;
-        uint64_t same = __ballot(v);
-        for (int b = 0; b < a.key_bits; ++b) {
-          const bool bit = v && ((j >> b) & 1);
-          const uint64_t bb = __ballot(bit);
-          same &= bit ? bb : ~bb;
+  int placed = 0;              // hits on the rows of earlier windows
+
+  for (int r0 = 0; r0 < Ld; r0 += W) {
+    const int nw = min(W, Ld - r0);
+    for (int j = tid; j < nw; j += 256) cur[j] = 0;
+    __syncthreads();
+    for (int64_t h = tid; h < H; h += 256) {
+      const int j = hit_row(a, e, h) - r0;
+      if (j >= 0 && j < nw) atomicAdd(&cur[j], 1);
+    }
+    __syncthreads();
+
+    // exclusive scan of the window's counts, in place; each thread owns a segment
+    const int seg = (nw + 255) / 256;
+    const int lo = min(tid * seg, nw), hi = min(lo + seg, nw);
+    int local = 0;
+    for (int j = lo; j < hi; ++j) local += cur[j];
+    int incl = local;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+      const int t = __shfl_up(incl, k);
+      if (lane >= k) incl += t;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int base = placed + incl - local;
+    for (int w = 0; w < wave; ++w) base += wtot[w];
+    for (int j = lo; j < hi; ++j) {
+      const int c = cur[j];
+      cur[j] = base;
+      roff[r0 + j] = base;
+      base += c;
+    }
+    placed += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    __syncthreads();
+
+    // stable placement: waves take turns over each group of 256 hits
+    for (int64_t h0 = 0; h0 < H; h0 += 256) {
+      for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+          const int64_t h = h0 + w * 64 + lane;
+          const int jr = h < H ? hit_row(a, e, h) : -1;
+          const bool v = jr >= r0 && jr < r0 + nw;
+          const int j = v ? jr - r0 : 0;
+          uint64_t same = __ballot(v);
+          for (int b = 0; b < a.key_bits; ++b) {
+            const bool bit = v && ((j >> b) & 1);
+            const uint64_t bb = __ballot(bit);
+            same &= bit ? bb : ~bb;
+          }
+          const int rank = __popcll(same & below);
+          const int count = __popcll(same);
+          const int pos = v ? cur[j] : 0;
+          __asm__ volatile("" ::: "memory");
+          if (v && pos + rank < H) {
+            int64_t qrow, p;
+            hit_qrow_pair(a, e, h, qrow, p);
+            out[pos + rank] = (int32_t)qrow;
+            a.sorted_g[el * H + pos + rank] = a.g[p];
+          }
+          if (v && rank == count - 1) cur[j] = pos + count;
         }
-        const int rank = __popcll(same & below);
-        const int count = __popcll(same);
-        const int pos = v ? cur[j] : 0;
-        __asm__ volatile("" ::: "memory");
-        if (v && pos + rank < H) {
-          int64_t qrow, p;
-          hit_qrow_pair(a, e, h, qrow, p);
-          out[pos + rank] = (int32_t)qrow;
-          a.sorted_g[el * H + pos + rank] = a.g[p];
-        }
-        if (v && rank == count - 1) cur[j] = pos + count;
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
+  if (tid == 0) roff[Ld] = placed;
 }
 
 // ---------------------------------------------------------------------------
@@ -1072,7 +1085,7 @@ static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t gs_lds, hipStr
       const size_t lds = (size_t)(4 * b.Ld + 4) * sizeof(int);
       hipLaunchKernelGGL(gradd_sort_waves_kernel, dim3((unsigned)b.nb), dim3(256), lds, s, b);
     } else {
-      const size_t lds = (size_t)(b.Ld + 4) * sizeof(int);
+      const size_t lds = (size_t)((b.Ld < kSortWin ? b.Ld : kSortWin) + 4) * sizeof(int);
       hipLaunchKernelGGL(gradd_sort_kernel, dim3((unsigned)b.nb), dim3(256), lds, s, b);
     }
     e = hipGetLastError();

@@ -118,19 +118,20 @@ def test_backward_rejects_invalid_arguments(L):
     assert bwd(L, argmax=None, wsb=need - 1) == LIK_ERR_INVALID_ARG
     assert "workspace too small" in L.lik_last_error().decode()
     # a document whose row table no longer fits in LDS goes to the workspace
-    # sort, whose row limit is 16000
+    # sort, which takes rows in windows and has no row limit: the call passes
+    # every shape check and stops only at the device check here
+    assert _lib.lik_plan_value(LIK_OP_BWD, (2, 32, 3, 40000, 128), LIK_BF16, 1, "gd_mode") == 0
     assert bwd(L, Ld=40000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
-    assert "sorts grad_D through the workspace" in L.lik_last_error().decode()
-    # 20000 rows still fit the LDS sort: the call passes every shape check and
-    # stops only at the device check here
+    assert "device" in L.lik_last_error().decode()
+    # 20000 rows still fit the LDS sort
     assert _lib.lik_plan_value(LIK_OP_BWD, (2, 32, 3, 20000, 128), LIK_BF16, 1, "gd_mode") == 1
     assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
     assert "device" in L.lik_last_error().decode()
 
 
-def test_long_pairwise_and_kd_backward_pass_the_row_limit(L):
-    # pairwise / kd stream grad_D rows, so Ld past the workspace sort's limit
-    # passes the row check; the calls then stop at the workspace check (no
+def test_long_pairwise_and_kd_backward_pass_the_shape_checks(L):
+    # pairwise / kd stream grad_D rows, so long documents pass the shape
+    # checks; the calls then stop at the workspace check (no
     # argmax given, so the forward is recomputed in a workspace that is too
     # small), before any device work on any machine
     st = L.lik_maxsim_pairwise_bwd(FAKE, FAKE, LIK_BF16, 2, 32, 40000, 128, None, None, FAKE,

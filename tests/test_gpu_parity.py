@@ -97,6 +97,31 @@ def test_kd_backward_past_the_sort_limit():
     full_check(_custom("kd-ld20000", "kd", "f16", Q, D, None, dm, g))
 
 
+def test_allpairs_backward_long_documents_workspace_sort_in_windows():
+    """All-pairs backward with Ld = 30000: the document's row table does not
+    fit in LDS, so grad_D is sorted through the workspace, in row windows of
+    16000.  Query tokens are copied into rows on both sides of the window edge
+    (15999, 16000) and near the end, so hits land in every window."""
+    from maxsim_scoring_02_amd import _lib
+
+    rng = np.random.default_rng(7009)
+    Nq, Lq, Nd, Ld, dim = 2, 32, 3, 30000, 128
+    assert _lib.lik_plan_value(_lib.LIK_OP_BWD, (Nq, Lq, Nd, Ld, dim), _lib.LIK_BF16, 1 | 2,
+                               "gd_mode") == 0
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    D = _rand_tokens(rng, (Nd, Ld, dim))
+    for d in range(Nd):
+        D[d, 15999] = Q[0, 3]
+        D[d, 16000] = Q[1, 5]
+        D[d, 29990] = Q[0, 7]
+        D[d, 100] = Q[1, 9]
+    dm = np.ones((Nd, Ld), dtype=bool)
+    dm[1, 20000:] = False                             # a masked tail
+    dm[2, :16001] = False                             # only the second window
+    g = rng.standard_normal((Nq, Nd))
+    full_check(_custom("ap-ld30000", "allpairs", "bf16", Q, D, None, dm, g))
+
+
 def _sub_pairwise(w, idx):
     return Workload(f"{w.name}-sample", "pairwise", w.dtype, w.Q[idx].contiguous(),
                     w.D[idx].contiguous(), None, None, None)

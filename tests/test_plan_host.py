@@ -183,7 +183,7 @@ int main() {
               fwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim, Nd % 2 == 0, true);
               fwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim, true);
               fwd_case(kKd, elem, Nq, Lq, 16, Ld, dim, false);
-              if (Ld <= 16000) bwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim);
+              bwd_case(kAllPairs, elem, Nq, Lq, Nd, Ld, dim);
               bwd_case(kPairwise, elem, Nq, Lq, 1, Ld, dim);
               bwd_case(kKd, elem, Nq, Lq, Nd % 32 + 1, Ld, dim);
             }
