@@ -404,6 +404,82 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     }
   };
   const int Ld = (int)a.Ld;
+  // Super-tiles are copied global -> LDS directly (no registers): the padded
+  // super-tile is kBlocks blocks of 1 KB, block q written by wave q % 4 as its
+  // (q / 4)-th load, lane l landing at byte 16 l of the block.  A lane's
+  // global offset inside the super-tile follows from that LDS position;
+  // lanes that land on row padding re-read offset 0.  One buffer descriptor
+  // per super-tile bounds the reads to the unit's rows (the rest read zero).
+  constexpr int kBlocks = kSTBytes / 1024;
+  static_assert(kSTBytes % 1024 == 0, "padded super-tile must be whole 1 KB blocks");
+  constexpr int kMyLoads = (kBlocks + kApNW - 1) / kApNW;   // per wave, at most
+  const int my_loads = (kBlocks - wave + kApNW - 1) / kApNW;
+  uint32_t voff[kMyLoads];
+#pragma unroll
+  for (int i = 0; i < kMyLoads; ++i) {
+    const int q = i * kApNW + wave;
+    const int bt = q * 1024 + lane * 16;                // byte in the padded super-tile
+    const int tile = bt / PD::kTileBytes, o = bt - tile * PD::kTileBytes;
+    const int row = o / PD::kStride, cb = o - row * PD::kStride;
+    voff[i] = (q < kBlocks && cb < G::kRowBytes)
+                  ? (uint32_t)((tile * kTile + row) * G::kRowBytes + cb)
+                  : 0u;
+  }
+  auto gload = [&](int meta, int unit, int stage) {
+    const int d = unit >> 8, c = unit & 0xff;
+    const int t = meta & 0xffffff;
+    const int t1 = min(c * tpc + tpc, (int)a.ntiles_max);
+    const char* base = (const char*)a.D + ((int64_t)d * Ld + (int64_t)t * kTile) * G::kRowBytes;
+    const int rows = min(t1 * kTile, Ld) - t * kTile;
+    const int nbytes = ((meta >> 27) & 1) ? min(rows, kSTRows) * G::kRowBytes : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+    char* dst = lds + stage * kSTBytes;
+#pragma unroll
+    for (int i = 0; i < kMyLoads; ++i) {
+      if (i < my_loads)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + (i * kApNW + wave) * 1024), 16,
+            (int)voff[i], 0, 0, 0);
+    }
+  };
+  constexpr int NST = ap_stages<E, DIM>();
+  // wait until this wave's loads for the next entry are in LDS (with three
+  // stages the loads issued this step, for the entry after, stay in flight)
+  auto wait_stage = [&]() {
+    if constexpr (NST == 3) {
+      if (my_loads == kMyLoads) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads - 1));
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+  };
+
+
+  // Before the set-up: the first unit's first super-tile (the schedule's
+  // first entry is always that tile; when the unit turns out empty the
+  // entry does not read it) and this wave's query fragments, so their
+  // latency overlaps the set-up's reads.
+  {
+    int d0, c0;
+    unit_dc(0, d0, c0);
+    gload((c0 * tpc) | (1 << 27), (d0 << 8) | c0, 0);
+  }
+  u32x4 bf[NB][G::kKSteps];
+  {
+    int64_t rows[NB];
+    bool ok[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      int64_t q, i;
+      ok[b] = slot_of(b * 32 + r, q, i);
+      rows[b] = ok[b] ? q * a.Lq + i : 0;
+    }
+    load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
+  }
   __shared__ int s_meta[kApMaxST];     // t | two << 24 | start << 25 | end << 26 | has << 27
   __shared__ int s_unit[kApMaxST];     // d << 8 | chunk
   __shared__ uint32_t s_w0[kApMaxST], s_w1[kApMaxST];
@@ -488,77 +564,13 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   lds_barrier();
   const int S = s_uoff[kApMaxDocs];
 
-  // Super-tiles are copied global -> LDS directly (no registers): the padded
-  // super-tile is kBlocks blocks of 1 KB, block q written by wave q % 4 as its
-  // (q / 4)-th load, lane l landing at byte 16 l of the block.  A lane's
-  // global offset inside the super-tile follows from that LDS position;
-  // lanes that land on row padding re-read offset 0.  One buffer descriptor
-  // per super-tile bounds the reads to the unit's rows (the rest read zero).
-  constexpr int kBlocks = kSTBytes / 1024;
-  static_assert(kSTBytes % 1024 == 0, "padded super-tile must be whole 1 KB blocks");
-  constexpr int kMyLoads = (kBlocks + kApNW - 1) / kApNW;   // per wave, at most
-  const int my_loads = (kBlocks - wave + kApNW - 1) / kApNW;
-  uint32_t voff[kMyLoads];
-#pragma unroll
-  for (int i = 0; i < kMyLoads; ++i) {
-    const int q = i * kApNW + wave;
-    const int bt = q * 1024 + lane * 16;                // byte in the padded super-tile
-    const int tile = bt / PD::kTileBytes, o = bt - tile * PD::kTileBytes;
-    const int row = o / PD::kStride, cb = o - row * PD::kStride;
-    voff[i] = (q < kBlocks && cb < G::kRowBytes)
-                  ? (uint32_t)((tile * kTile + row) * G::kRowBytes + cb)
-                  : 0u;
-  }
-  auto gload = [&](int meta, int unit, int stage) {
-    const int d = unit >> 8, c = unit & 0xff;
-    const int t = meta & 0xffffff;
-    const int t1 = min(c * tpc + tpc, (int)a.ntiles_max);
-    const char* base = (const char*)a.D + ((int64_t)d * Ld + (int64_t)t * kTile) * G::kRowBytes;
-    const int rows = min(t1 * kTile, Ld) - t * kTile;
-    const int nbytes = ((meta >> 27) & 1) ? min(rows, kSTRows) * G::kRowBytes : 0;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
-    char* dst = lds + stage * kSTBytes;
-#pragma unroll
-    for (int i = 0; i < kMyLoads; ++i) {
-      if (i < my_loads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + (i * kApNW + wave) * 1024), 16,
-            (int)voff[i], 0, 0, 0);
-    }
-  };
-  constexpr int NST = ap_stages<E, DIM>();
-  // wait until this wave's loads for the next entry are in LDS (with three
-  // stages the loads issued this step, for the entry after, stay in flight)
-  auto wait_stage = [&]() {
-    if constexpr (NST == 3) {
-      if (my_loads == kMyLoads) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads - 1));
-      }
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-  };
-
-  // prologue: the first entries' tiles, the query fragments and the query
-  // mask are all requested before any is waited for
-  if (S > 0) gload(__builtin_amdgcn_readfirstlane(s_meta[0]), __builtin_amdgcn_readfirstlane(s_unit[0]), 0);
-  if (NST == 3 && S > 1)
+  // prologue: the second entry's tiles go out now; the first entry's
+  // tiles and the query fragments, requested before the set-up, are older
+  // than them, so waiting with only the second entry's loads in flight
+  // covers both
+  const bool second = NST == 3 && S > 1;
+  if (second)
     gload(__builtin_amdgcn_readfirstlane(s_meta[1]), __builtin_amdgcn_readfirstlane(s_unit[1]), 1);
-  u32x4 bf[NB][G::kKSteps];
-  {
-    int64_t rows[NB];
-    bool ok[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      int64_t q, i;
-      ok[b] = slot_of(b * 32 + r, q, i);
-      rows[b] = ok[b] ? q * a.Lq + i : 0;
-    }
-    load_bfrags<E, DIM, NB>(bf, (const char*)a.Q, rows, ok, h);
-  }
   // this lane's output slot, fixed for the whole kernel
   const int L = NB == 2 ? lane : (lane & 31);
   const bool writer = NB == 2 || lane < 32;
@@ -571,7 +583,15 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   const bool fast_sum = a.qpw > 0 && a.Lq == 32;
   const int64_t score_base = slot_q * a.n_docs;
   const int64_t part_lane = (int64_t)gw * SPW + L;
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (second) {
+    if (my_loads == kMyLoads) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads - 1));
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
   lds_barrier();
 
   const int a_off = r * PD::kStride + h * 16;
