@@ -657,18 +657,26 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     for (int b = 0; b < NB; ++b) asm volatile("" : "=v"(Xa[b]), "=v"(Xb[b]));
     if (step) {
       const char* buf = lds + cur * kSTBytes;
-      if (two) {
-        if (word0 == kFull && word1 == kFull) {
-          mfma_pair_run<E, DIM, NB, true>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, Xa[0],
-                                          Xb[0]);
-        } else {
-          f32x16 ca, cb;                 // a full word gives an all-zero init
-          tile_init_uniform(ca, word0);
-          tile_init_uniform(cb, word1);
-          mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb);
-        }
-      } else {
+      // With the argmax kept and two column blocks, a single-tile step runs
+      // as a pair whose second tile is wholly masked (word 0: every row
+      // starts at -inf and never wins): with a single-tile path the two
+      // paths' accumulators met in different registers and every pair step
+      // paid 32 register copies (in-batch text 111.4 -> 109.7 us, pages
+      // 94.7 -> 92.8).  The max-only fold and the one-block kernels have no
+      // such join cost and keep the single-tile path (long documents: 703
+      // against 730 us).
+      constexpr bool kPairsOnly = KEEP && NB == 2;
+      const uint32_t w1 = two ? word1 : 0u;
+      if (!kPairsOnly && !two) {
         tile_mfma(Xa, buf, word0);
+      } else if (word0 == kFull && w1 == kFull) {
+        mfma_pair_run<E, DIM, NB, true>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, Xa[0],
+                                        Xb[0]);
+      } else {
+        f32x16 ca, cb;                 // a full word gives an all-zero init
+        tile_init_uniform(ca, word0);
+        tile_init_uniform(cb, w1);
+        mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb);
       }
     }
     // One fold per step on every path, so the argmax state has a single
