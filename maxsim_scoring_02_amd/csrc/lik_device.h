@@ -250,6 +250,24 @@ __device__ __forceinline__ void sel_copy8(float (&dst)[16], const f32x16& a, con
         [a7] "v"(a[O + 7]), [b7] "v"(b[O + 7]));
 }
 
+// (mask bit of this lane ? b : a), one select under a wave-uniform lane mask.
+__device__ __forceinline__ float sel_mask(float a, float b, uint64_t mask) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+__device__ __forceinline__ int sel_mask_i(int a, int b, uint64_t mask) {
+  int r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+// (mask bit of this lane ? 1 : 0)
+__device__ __forceinline__ int mask_bit(uint64_t mask) {
+  int r;
+  asm("v_cndmask_b32_e64 %0, 0, 1, %1" : "=v"(r) : "s"(mask));
+  return r;
+}
+
 // Start of a unit: only the running max and the tile are reset.  The 16
 // values are written by the first fold that improves on -inf; a lane that
 // never improves (no valid row of its half in the unit) keeps run_max = -inf,
@@ -267,12 +285,12 @@ __device__ __forceinline__ void state_fold_step(BlockState& s, const f32x16& xa,
   const float ta = max16_lean(xa);
   const float tb = two ? max16_lean(xb) : -__builtin_inff();
   const float tm = vmax2(ta, tb);
-  const bool better = step && tm > s.run_max;
-  const bool useb = tb > ta;
-  const uint64_t lanes = __builtin_amdgcn_ballot_w64(better);
-  const uint64_t ub = __builtin_amdgcn_ballot_w64(useb);
-  s.run_max = better ? tm : s.run_max;
-  s.best_tile = better ? t + (int)useb : s.best_tile;
+  // lane masks straight from the compares (step is uniform), and the state
+  // updated by selects under them
+  const uint64_t lanes = step ? __builtin_amdgcn_ballot_w64(tm > s.run_max) : 0ull;
+  const uint64_t ub = __builtin_amdgcn_ballot_w64(tb > ta);
+  s.run_max = sel_mask(s.run_max, tm, lanes);
+  s.best_tile = sel_mask_i(s.best_tile, t + mask_bit(ub), lanes);
   sel_copy8<0>(s.best_val, xa, xb, lanes, ub);
   sel_copy8<8>(s.best_val, xa, xb, lanes, ub);
 }

@@ -615,6 +615,8 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     Xa[b] = f32x16{};
     Xb[b] = f32x16{};
   }
+  // a lone tile runs as a pair in these kernels (see the step below)
+  constexpr bool kPairsOnly = KEEP && NB == 2;
   int cur = 0;                                   // stage of entry e
   // schedule words are read one step ahead, so no LDS round trip stands
   // between a step's start and its first load or MFMA
@@ -665,7 +667,6 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
       // 94.7 -> 92.8).  The max-only fold and the one-block kernels have no
       // such join cost and keep the single-tile path (long documents: 703
       // against 730 us).
-      constexpr bool kPairsOnly = KEEP && NB == 2;
       const uint32_t w1 = two ? word1 : 0u;
       if (!kPairsOnly && !two) {
         tile_mfma(Xa, buf, word0);
@@ -684,7 +685,8 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
     // tiles folds nothing; a single-tile step ignores Xb.
     if constexpr (KEEP) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) state_fold_step(st[b], Xa[b], Xb[b], t, step, two);
+      for (int b = 0; b < NB; ++b)
+        state_fold_step(st[b], Xa[b], Xb[b], t, step, kPairsOnly || two);
     } else if (step) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
