@@ -9,7 +9,8 @@ steps, then exactly K timed steps between two device synchronisations, with
 one HIP event at each end of them and none in between; rank 0 prints one JSON
 line.  Two untimed passes follow: K steps with events between forward and
 backward (`config.fwd_ms`, `config.bwd_ms`) and K forwards with the
-library's events around its main kernel (`roofline.kernel_ms`).
+library's events attached to its main kernel's launch
+(`roofline.kernel_ms`).
 
 Default workload: ColBERT-text in-batch contrastive fwd+bwd -- 256 queries x
 32 tokens against 256 documents padded to 300 tokens (true lengths uniform in
@@ -495,8 +496,9 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
     torch.cuda.synchronize()
     fwd_ms = [a.elapsed_time(b) for a, b, _ in ev]
     bwd_ms = [b.elapsed_time(c) for _, b, c in ev]
-    # Kernel pass: HIP events recorded by the library around the main forward
-    # kernel on its own stream (the roofline's duration).
+    # Kernel pass: HIP events the library attaches to the main forward
+    # kernel's launch (they carry the kernel's own start and end: the
+    # roofline's duration).
     kev = HipEvents(op.L, steps)
     for k in range(steps):
         op.L.lik_set_profile_events(*kev.ev[k])
@@ -565,7 +567,7 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_ms": round(t_kern, 5),
-            "timed_as": "main forward kernel alone, HIP events recorded by the library on its stream",
+            "timed_as": "main forward kernel alone, HIP events attached to its launch by the library",
             # the whole step (every kernel of forward and backward) against
             # the same peak: `value` / `peak`
             "step_frac": round(value / peak, 4),

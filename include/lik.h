@@ -101,10 +101,11 @@ int lik_supported_dim(int64_t dim);
 
 /*
  * Profiling hook (not needed for scoring).  After this call, every forward
- * entry point called from the same host thread records `start_event` on its
- * stream just before it launches its main scoring kernel and `stop_event`
- * just after it (the mask preparation and split-merge kernels fall outside),
- * so that the main kernel's duration can be read with hipEventElapsedTime.
+ * entry point called from the same host thread attaches `start_event` and
+ * `stop_event` to the launch of its main scoring kernel (hipExtLaunchKernel:
+ * they take the kernel's own start and end; the mask preparation and
+ * split-merge kernels fall outside), so that the main kernel's duration can
+ * be read with hipEventElapsedTime.
  * Both are hipEvent_t handles owned by the caller, created on the current
  * device; pass NULL, NULL to stop.  Returns LIK_ERR_INVALID_ARG when exactly
  * one of them is NULL.

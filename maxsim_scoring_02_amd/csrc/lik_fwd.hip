@@ -14,6 +14,7 @@
 // document with no valid token scores -1e9, scores are float32.  The running
 // max is kept in registers and the similarity grid is never stored (social
 // thread, post (4/N)).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "lik_device.h"
@@ -1041,15 +1042,27 @@ __global__ __launch_bounds__(256) void combine_fwd_wave_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// Launch `kernel` with FwdArgs a; with the profiling events set, they are
+// attached to the launch itself (hipExtLaunchKernel), so they carry the
+// kernel's own start and end rather than the stream's position around it.
+template <class K>
+static hipError_t launch_fwd(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                             const FwdArgs& a) {
+  hipEvent_t ev0, ev1;
+  profile_events(&ev0, &ev1);
+  if (ev0 && ev1) {
+    FwdArgs copy = a;
+    void* args[] = {&copy};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, s,
+                              ev0, ev1, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
 template <Elem E, int DIM, int NB, bool MASK, bool KEEP>
 static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
-  hipEvent_t ev0, ev1;
-  profile_events(&ev0, &ev1);
-  if (ev0) {
-    hipError_t e = hipEventRecord(ev0, s);
-    if (e != hipSuccess) return e;
-  }
   if (p.layout == kAllPairs) {
     const int64_t grid = 8 * p.gpx * p.n_sb;
     constexpr int lds = ap_lds_bytes<E, DIM>();
@@ -1059,17 +1072,13 @@ static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t 
           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((allpairs_fwd_kernel<E, DIM, NB, MASK, KEEP>), dim3((unsigned)grid),
-                       dim3(kApThreads), lds, s, a);
-  } else {
-    constexpr int W = pr_waves<E, DIM>();
-    const int64_t grid = cdiv(p.n_units, W);
-    hipLaunchKernelGGL((pairs_fwd_kernel<E, DIM, NB, MASK>), dim3((unsigned)grid),
-                       dim3(W * kWave), W * G::kTileBytes, s, a);
+    return launch_fwd(allpairs_fwd_kernel<E, DIM, NB, MASK, KEEP>, dim3((unsigned)grid),
+                      dim3(kApThreads), lds, s, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
-  return e;
+  constexpr int W = pr_waves<E, DIM>();
+  const int64_t grid = cdiv(p.n_units, W);
+  return launch_fwd(pairs_fwd_kernel<E, DIM, NB, MASK>, dim3((unsigned)grid), dim3(W * kWave),
+                    W * G::kTileBytes, s, a);
 }
 
 template <Elem E, int DIM, int NB>
