@@ -72,16 +72,16 @@ struct BwdArgs {
 // ---------------------------------------------------------------------------
 // grad_Q: grid (query, token group); thread = (token, 16-byte chunk)
 // ---------------------------------------------------------------------------
-template <Elem E, int DIM>
-__global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
+// U gathered rows in flight per thread.
+template <Elem E, int DIM, int U>
+__device__ __forceinline__ void gradq_body(const BwdArgs& a, int64_t q, int64_t iblk) {
   using G = Geo<E, DIM>;
   constexpr int EPC = ElemInfo<E>::kPerChunk;
   constexpr int CPR = G::kCPR;
   constexpr int TPB = 256 / CPR;
   const int tid = threadIdx.x;
   const int tk = tid / CPR, c = tid - tk * CPR;
-  const int64_t q = blockIdx.x;
-  const int64_t i = (int64_t)blockIdx.y * TPB + tk;
+  const int64_t i = iblk * TPB + tk;
   if (i >= a.Lq) return;
   const bool ap = a.layout == kAllPairs;
   const int64_t K = ap ? a.n_docs : a.K;
@@ -89,9 +89,6 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
   float acc[EPC];
 #pragma unroll
   for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
-  // 16 gathered rows in flight per thread: the loop is bound by memory
-  // latency, not bandwidth, at the usual few-thousand-thread grids
-  constexpr int U = 16;
   for (int64_t k0 = 0; k0 < K; k0 += U) {
     int jj[U];
     float gg[U];
@@ -129,6 +126,13 @@ __global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < EPC; k += 4)
     *reinterpret_cast<float4*>(out + k) = make_float4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3]);
+}
+
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void gradq_kernel(BwdArgs a) {
+  // 16 gathered rows in flight per thread: the loop is bound by memory
+  // latency, not bandwidth, at the usual few-thousand-thread grids
+  gradq_body<E, DIM, 16>(a, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -942,7 +946,7 @@ template <> __device__ __forceinline__ void load4_as_float<Elem::F32>(const char
 
 
 template <Elem E, int DIM>
-__global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
+__device__ __forceinline__ void gradd_pairs_body(const BwdArgs& a, int64_t block) {
   constexpr int F4 = DIM / 4;                 // float4 per gradient row
   constexpr int RPI = F4 >= 64 ? 1 : 64 / F4; // rows per wave store
   constexpr int NH = kPairsMaxLq / 64;        // hit registers per lane
@@ -952,7 +956,7 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
   // gd_parts waves per document, each streaming a contiguous share of its
   // rows (whole stores of RPI rows), so enough stores are in flight
   const int parts = a.gd_parts;
-  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wv = block * 4 + (threadIdx.x >> 6);
   const int64_t e = wv / parts;
   const int part = (int)(wv - e * parts);
   if (e >= a.n_docs) return;
@@ -1017,6 +1021,30 @@ __global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f) = w;
       }
     }
+  }
+}
+
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void gradd_pairs_kernel(BwdArgs a) {
+  gradd_pairs_body<E, DIM>(a, blockIdx.x);
+}
+
+// Both gradients of the pairwise / kd layouts in one launch: the first
+// n_gq blocks gather grad_Q (bound by the latency of row gathers from HBM),
+// the rest stream grad_D (bound by HBM writes), so the gathers run under
+// the write stream instead of before it.  The two parts share no data.
+constexpr int kGqFusedRows = 4;
+template <Elem E, int DIM>
+__global__ __launch_bounds__(256) void grads_pairs_kernel(BwdArgs a, int64_t n_gq, int64_t n_iblk) {
+  const int64_t b = blockIdx.x;
+  if (b < n_gq) {
+    const int64_t q = b / n_iblk;
+    // fewer rows in flight than gradq_kernel: the registers stay within what
+    // the grad_D part needs for its full occupancy, and the gathers' latency
+    // is hidden by the write stream anyway
+    gradq_body<E, DIM, kGqFusedRows>(a, q, b - q * n_iblk);
+  } else {
+    gradd_pairs_body<E, DIM>(a, b - n_gq);
   }
 }
 
@@ -1108,6 +1136,16 @@ static hipError_t launch_gradd(const BwdArgs& a, int mode, size_t gs_lds, hipStr
 template <Elem E, int DIM>
 static hipError_t launch_grads(const BwdPlan& p, const BwdArgs& a, bool want_q, bool want_d,
                                hipStream_t s) {
+  if (want_q && want_d && !a.gq_ap && p.gd_mode == kGdPairs) {
+    using G = Geo<E, DIM>;
+    constexpr int TPB = 256 / G::kCPR;
+    const int64_t n_iblk = cdiv(a.Lq, TPB);
+    const int64_t n_gq = a.Nq * n_iblk;
+    const int64_t n_gd = cdiv(a.n_docs * a.gd_parts, 4);
+    hipLaunchKernelGGL((grads_pairs_kernel<E, DIM>), dim3((unsigned)(n_gq + n_gd)), dim3(256), 0,
+                       s, a, n_gq, n_iblk);
+    return hipGetLastError();
+  }
   if (want_q) {
     hipError_t e = launch_gradq<E, DIM>(a, s);
     if (e != hipSuccess) return e;
