@@ -276,7 +276,8 @@ template <Elem E, int DIM, int NB, bool ZERO>
 __device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB],
                                               const char* bufa, const char* bufb,
                                               const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
-                                              int a_off, const f32x16& ca, const f32x16& cb) {
+                                              int a_off, const f32x16& ca, const f32x16& cb,
+                                              bool twob = true) {
   using G = Geo<E, DIM>;
   constexpr int KS = G::kKSteps;
   constexpr int kWin = E == Elem::F32 ? 2 : (KS < 4 ? KS : 4);
@@ -295,10 +296,12 @@ __device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB]
       if (m == 0) xa[b] = mfma_first<E, ZERO>(aa[0], bf[b][0], ca);
       else mfma_chunk<E>(xa[b], aa[m], bf[b][m]);
     }
+    // without a second tile, its chains stop after the first K-step: every
+    // row started at -inf (cb), so -inf is already their final value
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (m == 0) xb[b] = mfma_first<E, ZERO>(ab[0], bf[b][0], cb);
-      else mfma_chunk<E>(xb[b], ab[m], bf[b][m]);
+      else if (twob) mfma_chunk<E>(xb[b], ab[m], bf[b][m]);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerChunk, 0);
     if (m + kWin < KS) {
@@ -678,7 +681,8 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
         f32x16 ca, cb;                 // a full word gives an all-zero init
         tile_init_uniform(ca, word0);
         tile_init_uniform(cb, w1);
-        mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb);
+        mfma_pair_run<E, DIM, NB, false>(Xa, Xb, buf, buf + PD::kTileBytes, bf, a_off, ca, cb,
+                                         two);
       }
     }
     // One fold per step on every path, so the argmax state has a single
