@@ -151,18 +151,40 @@ __device__ __forceinline__ void tile_init(f32x16& c, uint32_t word, int h) {
 
 // The same for a wave-uniform word: element v of the lanes in half h comes
 // from bit 8*(v/4) + 4*h + v%4, so each element is one select under a lane
-// mask built with scalar instructions (valid rows 0, masked rows -inf).
+// mask built with two scalar bit-field extracts straight into vcc (valid
+// rows 0, masked rows -inf).
+template <int V>
+__device__ __forceinline__ float tile_init_elem(uint32_t word, float ninf, float zero) {
+  constexpr int b0 = 8 * (V >> 2) + (V & 3);
+  float r;
+  // vcc = (bit b0 of word ? all of lanes 0-31) | (bit b0+4 ? all of 32-63):
+  // two sign-extended 1-bit fields, one per half of vcc
+  asm("s_bfe_i32 vcc_lo, %1, %4\n\t"
+      "s_bfe_i32 vcc_hi, %1, %5\n\t"
+      "v_cndmask_b32_e32 %0, %2, %3, vcc"
+      : "=v"(r)
+      : "s"(word), "v"(ninf), "v"(zero), "i"(b0 | (1 << 16)), "i"((b0 + 4) | (1 << 16))
+      : "vcc");
+  return r;
+}
 __device__ __forceinline__ void tile_init_uniform(f32x16& c, uint32_t word) {
-  const float ninf = -__builtin_inff();
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int b0 = 8 * (v >> 2) + (v & 3);
-    const uint64_t keep = (((word >> b0) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                          (((word >> (b0 + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-    float r;
-    asm("v_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(r) : "v"(ninf), "s"(keep));
-    c[v] = r;
-  }
+  const float ninf = -__builtin_inff(), zero = 0.0f;
+  c[0] = tile_init_elem<0>(word, ninf, zero);
+  c[1] = tile_init_elem<1>(word, ninf, zero);
+  c[2] = tile_init_elem<2>(word, ninf, zero);
+  c[3] = tile_init_elem<3>(word, ninf, zero);
+  c[4] = tile_init_elem<4>(word, ninf, zero);
+  c[5] = tile_init_elem<5>(word, ninf, zero);
+  c[6] = tile_init_elem<6>(word, ninf, zero);
+  c[7] = tile_init_elem<7>(word, ninf, zero);
+  c[8] = tile_init_elem<8>(word, ninf, zero);
+  c[9] = tile_init_elem<9>(word, ninf, zero);
+  c[10] = tile_init_elem<10>(word, ninf, zero);
+  c[11] = tile_init_elem<11>(word, ninf, zero);
+  c[12] = tile_init_elem<12>(word, ninf, zero);
+  c[13] = tile_init_elem<13>(word, ninf, zero);
+  c[14] = tile_init_elem<14>(word, ninf, zero);
+  c[15] = tile_init_elem<15>(word, ninf, zero);
 }
 
 // Fold one (masked) tile's accumulator into the running state, branch-free.
