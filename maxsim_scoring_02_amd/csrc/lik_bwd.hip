@@ -144,7 +144,8 @@ template <int CPR, int U>
 __device__ __forceinline__ int grp_bcast(int v, int base_lane) {
   if constexpr (CPR == 16) {
     (void)base_lane;
-    return __builtin_amdgcn_update_dpp(0, v, 0x150 + U, 0xf, 0xf, false);
+    // every lane reads a valid source lane, so bound_ctrl needs no old value
+    return __builtin_amdgcn_update_dpp(0, v, 0x150 + U, 0xf, 0xf, true);
   } else {
     return __shfl(v, base_lane + U);
   }
@@ -799,31 +800,35 @@ __global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
   const int lo = range_lo(grp), hi = range_lo(grp + 1);
   const __amdgpu_buffer_rsrc_t qrs = buf_rsrc(a.Q, (uint32_t)((int64_t)Nq * Lq * G::kRowBytes));
   const uint32_t my_chunk = (uint32_t)c * 16u;
-  float acc[EPC], head[EPC];
+  float acc[EPC];
 #pragma unroll
-  for (int k = 0; k < EPC; ++k) acc[k] = head[k] = 0.0f;
+  for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
   int cur_row = lo < hi ? (int)(sorted[lo] >> 16) : -1;
   bool in_head = lo < hi && start[cur_row] < lo;   // first row began in an earlier range
-  bool have_head = false;
   auto store_row = [&](int row, const float (&v)[EPC]) {
     float* out = gD_doc + (int64_t)row * DIM + c * EPC;
 #pragma unroll
     for (int k = 0; k < EPC; k += 4)
       *reinterpret_cast<float4*>(out + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
   };
-  // a row ended inside the range: the head (begun earlier) is kept, any
-  // other row is whole and stored
+  // the head (a row begun in an earlier range) goes to this group's first
+  // LDS partial slot, for the group where the row starts
+  auto write_head = [&](const float (&v)[EPC]) {
+    float* out = part + (grp * 2) * DIM + c * EPC;
+#pragma unroll
+    for (int k = 0; k < EPC; k += 4)
+      *reinterpret_cast<float4*>(out + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  };
+  // a row ended inside the range: the head is kept, any other row is whole
+  // and stored.  Only stores here: the caller clears acc with selects, so the
+  // accumulators keep one register assignment on both sides of the branch.
   auto end_row = [&]() {
     if (in_head) {
-#pragma unroll
-      for (int k = 0; k < EPC; ++k) head[k] = acc[k];
-      have_head = true;
+      write_head(acc);
       in_head = false;
     } else {
       store_row(cur_row, acc);
     }
-#pragma unroll
-    for (int k = 0; k < EPC; ++k) acc[k] = 0.0f;
   };
   for (int p = lo; p < hi; p += R) {
     // lane u (< R) of the group prepares sorted entry p + u; entries past the
@@ -858,10 +863,11 @@ __global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
     } else {
       static_for<R>([&](auto u) {
         const int r = grp_bcast<CPR, u>(row_c, base_lane);
-        if (r != cur_row) {
-          end_row();
-          cur_row = r;
-        }
+        const bool chg = r != cur_row;
+        if (chg) end_row();
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) acc[k] = chg ? 0.0f : acc[k];
+        cur_row = chg ? r : cur_row;
         add(ch[u], grp_bcast_f<CPR, u>(g_c, base_lane));
       });
     }
@@ -871,9 +877,7 @@ __global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
   int tail_row = -1;
   if (cur_row >= 0) {
     if (in_head) {
-#pragma unroll
-      for (int k = 0; k < EPC; ++k) head[k] = acc[k];
-      have_head = true;
+      write_head(acc);
     } else if (start[cur_row + 1] > hi) {
       tail_row = cur_row;
       float* out = part + (grp * 2 + 1) * DIM + c * EPC;
@@ -883,12 +887,6 @@ __global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
     } else {
       store_row(cur_row, acc);
     }
-  }
-  if (have_head) {
-    float* out = part + (grp * 2) * DIM + c * EPC;
-#pragma unroll
-    for (int k = 0; k < EPC; k += 4)
-      *reinterpret_cast<float4*>(out + k) = make_float4(head[k], head[k + 1], head[k + 2], head[k + 3]);
   }
   __syncthreads();
 
