@@ -676,18 +676,25 @@ __global__ __launch_bounds__(kGsThreads) void gradd_sorted_kernel(BwdArgs a) {
     int* hw = hist + wave * Ld;
     unsigned long long* mw = masks + wave * Ld;
     constexpr int UL = 8;                        // chunks whose argmax loads are in flight together
+    // argmax[(q * Nd + e) * Lq + i] for hit h = q * Lq + i is
+    // argmax[q * (Nd - 1) * Lq + e * Lq + h]
+    const uint64_t q_stride = (uint64_t)(Nd - 1) * (uint64_t)Lq;
+    const int32_t* am_e = a.argmax + e * (int64_t)Lq;
     for (int hb = h0; hb < h1; hb += 64 * UL) {
+      // every load is issued before any is used: hits past the range read
+      // the range's last hit and are dropped afterwards
+      int raw[UL];
+#pragma unroll
+      for (int u = 0; u < UL; ++u) {
+        const int hc = min(hb + 64 * u + lane, h1 - 1);
+        const uint32_t q = (uint32_t)div_lq(hc, a.lq_magic);
+        raw[u] = am_e[q * q_stride + (uint32_t)hc];
+      }
       int jj[UL];
 #pragma unroll
       for (int u = 0; u < UL; ++u) {
-        const int h = hb + 64 * u + lane;
-        jj[u] = (int)kNoKey;
-        if (h < h1) {
-          const int q = div_lq(h, a.lq_magic);
-          const int i = h - q * Lq;
-          const int j = a.argmax[((int64_t)q * Nd + e) * Lq + i];
-          if (j >= 0 && j < Ld) jj[u] = j;
-        }
+        const bool ok = hb + 64 * u + lane < h1 && raw[u] >= 0 && raw[u] < Ld;
+        jj[u] = ok ? raw[u] : (int)kNoKey;
       }
 #pragma unroll
       for (int u = 0; u < UL; ++u) {
