@@ -32,7 +32,12 @@ long-rerank, or `all` (one line each); `next` runs the long-context backward
 upstream grad, forward + backward), kd-loss-head (the kd-candidates
 inputs with the negative-doc cross-entropy as the loss head) and
 inbatch-text-f32 (the in-batch text step with float32 inputs, computed
-exactly on the fp32 MFMA and reported against its 157.3 TFLOP/s peak);
+exactly on the fp32 MFMA and reported against its 157.3 TFLOP/s peak) and
+inbatch-text-f32x3 (the same float32 inputs through LIK_F32_BF16X3: the
+forward splits every value into bfloat16 high and low parts and takes three
+bfloat16 MFMA products per element pair; `value` counts the float32 MaxSim
+flops, the kernel roofline the three bfloat16 products per pair against the
+2.5 PFLOP/s bfloat16 peak);
 `loss-sweep` runs the loss head over batch x negatives, one line per point
 kd-loss-head-b{64,128,256}-n{2,4,8,16}: kd forward with Lq 32 and Ld 1030 in
 bf16, the negative-doc cross-entropy, and the backward, with the step's
@@ -148,7 +153,8 @@ class Op:
         self.D = w.D.to(dev).contiguous()
         self.qm = None if w.q_mask is None else w.q_mask.to(dev).contiguous().view(torch.uint8)
         self.dm = None if w.d_mask is None else w.d_mask.to(dev).contiguous().view(torch.uint8)
-        self.dt = _lib.DTYPE_CODE[self.Q.dtype]
+        self.dt = (_lib.LIK_F32_BF16X3 if w.meta.get("fp32_split")
+                   else _lib.DTYPE_CODE[self.Q.dtype])
         self.backward = backward
         Lq, dim = w.Q.shape[1], w.dim
         shape = w.scores_shape
@@ -295,6 +301,12 @@ def make_workload(name: str):
         w = wl.inbatch_text(dtype="f32")
         w.name = name
         return w, True
+    if name == "inbatch-text-f32x3":
+        # the same float32 inputs scored through split bfloat16 parts
+        w = wl.inbatch_text(dtype="f32")
+        w.name = name
+        w.meta["fp32_split"] = True
+        return w, True
     if name == "kd-loss-head":
         # the pages' loss-head benchmark shape (B 256 x 16 candidates, Lq 32,
         # Ld 1030): kd forward, negative-doc cross-entropy with candidate 0
@@ -350,6 +362,7 @@ DOMINANT = {  # kernel whose roofline is reported, and its bound
     "long-rerank-bwd": ("pairs_fwd", "hbm"),
     "kd-loss-head": ("pairs_fwd", "hbm"),
     "inbatch-text-f32": ("allpairs_fwd", "mfma"),
+    "inbatch-text-f32x3": ("allpairs_fwd", "mfma"),
 }
 
 
@@ -512,12 +525,14 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
     t_kern = float(np.mean(kern_ms))
     kern, bound = DOMINANT.get(name, ("pairs_fwd", "hbm") if name.startswith("kd-loss-head-b")
                                else (None, None))
+    split = bool(w.meta.get("fp32_split"))
     if bound == "mfma":
         flops = f_fwd + (f_bwd if backward else 0.0)
         value = flops / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        achieved = f_fwd / (t_kern * 1e-3) / 1e12
-        peak = PEAK_MFMA_F32 if w.dtype == "f32" else PEAK_MFMA_16BIT
+        # the split forward's own work: three bfloat16 products per pair
+        achieved = (3.0 if split else 1.0) * f_fwd / (t_kern * 1e-3) / 1e12
+        peak = PEAK_MFMA_F32 if (w.dtype == "f32" and not split) else PEAK_MFMA_16BIT
         rl_unit = "TFLOP/s"
     else:
         nbytes = b_fwd + (b_bwd if backward else 0.0)
@@ -538,7 +553,7 @@ def bench_one(name: str, steps: int, warmup: int, with_cpu: bool, dump_dir=None)
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "f32-bf16x3" if split else w.dtype,
         "data": "synthetic (seeded; shapes of the pages' workloads)",
         "config": {
             "workload": name,
@@ -632,7 +647,8 @@ def main():
         copy_calibration(args.copy_calibration, max(args.steps, 1))
         return
     groups = {"all": ["inbatch-text", "inbatch-pages", "kd-candidates", "long-docs", "long-rerank"],
-              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head", "inbatch-text-f32"],
+              "next": ["long-docs-bwd", "long-rerank-bwd", "kd-loss-head", "inbatch-text-f32",
+                       "inbatch-text-f32x3"],
               "loss-sweep": LOSS_SWEEP}
     names = groups.get(args.workload, [args.workload])
     for i, name in enumerate(names):

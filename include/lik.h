@@ -47,8 +47,10 @@
  *                         too small;
  *   LIK_ERR_UNSUPPORTED   a valid request the library does not implement
  *                         (see lik_supported_dim; all-pairs with
- *                         Nd >= 2^23, Ld > 261120 or Nq * Lq > 2^30; no
- *                         gfx950 device);
+ *                         Nd >= 2^23, Ld > 261120 or Nq * Lq > 2^30;
+ *                         LIK_F32_BF16X3 where the all-pairs forward's
+ *                         split copies, (Nq*Lq + Nd*Ld) * dim * 4 bytes,
+ *                         exceed 1 GiB; no gfx950 device);
  *   LIK_ERR_HIP           a HIP launch error, reported as it happens.
  *   Zero-sized batches (Nq, Nd, B or N of 0) are a successful no-op.
  * Determinism.  For identical inputs and shapes the results are bitwise
@@ -68,7 +70,26 @@ extern "C" {
 
 #define LIK_ABI_VERSION 1
 
-typedef enum { LIK_F16 = 0, LIK_BF16 = 1, LIK_F32 = 2 } lik_dtype;
+/*
+ * Input element types.  LIK_F16, LIK_BF16 and LIK_F32 are the input types of
+ * the README's "Precision and compatibility" section, multiplied exactly
+ * (every product of two inputs is exact) with float32 accumulation.
+ *
+ * LIK_F32_BF16X3 takes the same float32 inputs and buffers as LIK_F32 and
+ * trades a bounded error for speed in the one place where float32 is slow:
+ * the all-pairs forward at dim 64 and 128 (also when a backward recomputes
+ * the argmax).  There every value x is split into two bfloat16 parts,
+ * hi = bf16(x) and lo = bf16(x - hi) (rounded to nearest even), in copies of
+ * Q and D kept in the workspace, and each product q*d is taken as
+ * hi_q*hi_d + hi_q*lo_d + lo_q*hi_d on the bfloat16 matrix cores with float32
+ * accumulation.  The dropped terms bound a similarity's error by about
+ * 3 * 2^-16 * sum_k |q_k d_k| beyond float32 accumulation (4.6e-5 for unit
+ * vectors); a score, a sum of Lq maxima, by Lq times that.  Values whose
+ * bfloat16 rounding overflows become infinite.  Every other call with
+ * LIK_F32_BF16X3 (pairwise and kd, dim 256, the gradient sums) computes
+ * exactly as LIK_F32: those kernels are bound by memory, not multiplies.
+ */
+typedef enum { LIK_F16 = 0, LIK_BF16 = 1, LIK_F32 = 2, LIK_F32_BF16X3 = 3 } lik_dtype;
 
 typedef enum {
   LIK_OK = 0,
@@ -144,7 +165,8 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq,
  *            "nchunks" (pieces a document is split into), "tpc" (32-row
  *            tiles per piece), "compact" (query tokens compacted), "partial"
  *            (per-piece partials merged by a second kernel), "qpw" (whole
- *            queries per wave, 0 = flattened), "n_units" (pairwise/kd waves);
+ *            queries per wave, 0 = flattened), "n_units" (pairwise/kd waves),
+ *            "split" (1 when LIK_F32_BF16X3 scores through split rows);
  *   backward every forward key (the plan of the recomputing forward) and
  *            "gd_mode" (grad_D kernel: 0 workspace sort, 1 sorted in LDS
  *            per all-pairs document, 2 pairwise/kd streaming), "gd_parts",

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "liblik.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG), "include", "lik.h")
 
 LIK_OK, LIK_ERR_INVALID_ARG, LIK_ERR_UNSUPPORTED, LIK_ERR_HIP = 0, 1, 2, 3
-LIK_F16, LIK_BF16, LIK_F32 = 0, 1, 2
+LIK_F16, LIK_BF16, LIK_F32, LIK_F32_BF16X3 = 0, 1, 2, 3
 (LIK_OP_FWD, LIK_OP_BWD, LIK_OP_PAIRWISE_FWD, LIK_OP_PAIRWISE_BWD,
  LIK_OP_KD_FWD, LIK_OP_KD_BWD) = range(6)
 
@@ -101,7 +101,9 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _embeddings(Q: torch.Tensor, D: torch.Tensor) -> int:
+def _embeddings(Q: torch.Tensor, D: torch.Tensor, fp32_split: bool = False) -> int:
+    """dtype code of the inputs; fp32_split asks for LIK_F32_BF16X3 (float32
+    inputs scored through bfloat16 high/low parts, see include/lik.h)."""
     if not (Q.is_cuda and D.is_cuda):
         raise ValueError("Q and D must be GPU tensors")
     if Q.device != D.device:
@@ -112,6 +114,10 @@ def _embeddings(Q: torch.Tensor, D: torch.Tensor) -> int:
         raise ValueError("Q and D must share the embedding dim")
     if not (Q.is_contiguous() and D.is_contiguous()):
         raise ValueError("Q and D must be contiguous")
+    if fp32_split:
+        if Q.dtype != torch.float32:
+            raise ValueError("fp32_split applies to float32 inputs only")
+        return LIK_F32_BF16X3
     return DTYPE_CODE[Q.dtype]
 
 
@@ -159,10 +165,10 @@ def lik_plan_value(op: int, dims, dtype: int, flags: int, key: str) -> int:
     return int(lib().lik_plan_value(op, *dims, dtype, flags, key.encode()))
 
 
-def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
+def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True, fp32_split=False):
     """All-pairs: Q [Nq, Lq, dim] x D [Nd, Ld, dim] -> scores [Nq, Nd] float32,
     argmax [Nq, Nd, Lq] int32 (or None)."""
-    dt = _embeddings(Q, D)
+    dt = _embeddings(Q, D, fp32_split)
     Nq, Lq, dim = Q.shape
     Nd, Ld, _ = D.shape
     qm = _mask(q_mask, (Nq, Lq), Q.device)
@@ -178,11 +184,11 @@ def lik_maxsim_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     return scores, am
 
 
-def lik_maxsim_fwd_noalloc(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
+def lik_maxsim_fwd_noalloc(Q, D, q_mask=None, d_mask=None, keep_argmax=True, fp32_split=False):
     """All-pairs forward through the allocation-free entry point: the library
     takes its scratch from a fixed per-device array (the outputs are still
     the caller's, allocated here)."""
-    dt = _embeddings(Q, D)
+    dt = _embeddings(Q, D, fp32_split)
     Nq, Lq, dim = Q.shape
     Nd, Ld, _ = D.shape
     qm = _mask(q_mask, (Nq, Lq), Q.device)
@@ -195,10 +201,10 @@ def lik_maxsim_fwd_noalloc(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     return scores, am
 
 
-def lik_maxsim_pairwise_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
+def lik_maxsim_pairwise_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True, fp32_split=False):
     """Pairwise: Q [B, Lq, dim] x D [B, Ld, dim] -> scores [B], argmax [B, Lq]."""
     _same_batch(Q, D, "pairwise")
-    dt = _embeddings(Q, D)
+    dt = _embeddings(Q, D, fp32_split)
     B, Lq, dim = Q.shape
     _, Ld, _ = D.shape
     qm = _mask(q_mask, (B, Lq), Q.device)
@@ -214,10 +220,10 @@ def lik_maxsim_pairwise_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
     return scores, am
 
 
-def lik_maxsim_kd_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True):
+def lik_maxsim_kd_fwd(Q, D, q_mask=None, d_mask=None, keep_argmax=True, fp32_split=False):
     """kd: Q [B, Lq, dim] x D [B, N, Ld, dim] -> scores [B, N], argmax [B, N, Lq]."""
     _same_batch(Q, D, "kd")
-    dt = _embeddings(Q, D)
+    dt = _embeddings(Q, D, fp32_split)
     B, Lq, dim = Q.shape
     _, N, Ld, _ = D.shape
     qm = _mask(q_mask, (B, Lq), Q.device)
@@ -251,8 +257,8 @@ def _argmax_in(am: Optional[torch.Tensor], shape, device) -> Optional[torch.Tens
 
 
 def lik_maxsim_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
-                   need_grad_q=True, need_grad_d=True) -> Tuple:
-    dt = _embeddings(Q, D)
+                   need_grad_q=True, need_grad_d=True, fp32_split=False) -> Tuple:
+    dt = _embeddings(Q, D, fp32_split)
     Nq, Lq, dim = Q.shape
     Nd, Ld, _ = D.shape
     qm = _mask(q_mask, (Nq, Lq), Q.device)
@@ -270,9 +276,9 @@ def lik_maxsim_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
 
 
 def lik_maxsim_pairwise_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
-                            need_grad_q=True, need_grad_d=True) -> Tuple:
+                            need_grad_q=True, need_grad_d=True, fp32_split=False) -> Tuple:
     _same_batch(Q, D, "pairwise")
-    dt = _embeddings(Q, D)
+    dt = _embeddings(Q, D, fp32_split)
     B, Lq, dim = Q.shape
     _, Ld, _ = D.shape
     qm = _mask(q_mask, (B, Lq), Q.device)
@@ -291,9 +297,9 @@ def lik_maxsim_pairwise_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=
 
 
 def lik_maxsim_kd_bwd(Q, D, grad_scores, argmax=None, q_mask=None, d_mask=None,
-                      need_grad_q=True, need_grad_d=True) -> Tuple:
+                      need_grad_q=True, need_grad_d=True, fp32_split=False) -> Tuple:
     _same_batch(Q, D, "kd")
-    dt = _embeddings(Q, D)
+    dt = _embeddings(Q, D, fp32_split)
     B, Lq, dim = Q.shape
     _, N, Ld, _ = D.shape
     qm = _mask(q_mask, (B, Lq), Q.device)

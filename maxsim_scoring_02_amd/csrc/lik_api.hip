@@ -59,7 +59,6 @@ int64_t mul_ok(std::initializer_list<int64_t> xs) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int elem_bytes(lik_dtype t) { return t == LIK_F32 ? 4 : 2; }
 
 std::atomic<int> g_dev_ok[64];   // 0 unknown, 1 gfx950, 2 other
 
@@ -89,7 +88,7 @@ struct Shapes {
 };
 
 lik_status check_shapes(lik_dtype dtype, Shapes& s) {
-  if (dtype != LIK_F16 && dtype != LIK_BF16 && dtype != LIK_F32)
+  if (dtype != LIK_F16 && dtype != LIK_BF16 && dtype != LIK_F32 && dtype != LIK_F32_BF16X3)
     return fail(LIK_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (s.nq_or_b < 0 || s.Lq < 0 || s.nd_or_n < 0 || s.Ld < 0 || s.dim < 0)
     return fail(LIK_ERR_INVALID_ARG, "negative size");
@@ -129,6 +128,19 @@ lik_status check_supported(lik_dtype dtype, const Shapes& s) {
   return LIK_OK;
 }
 
+// LIK_F32_BF16X3 on the all-pairs forward: the split copies of Q and D live
+// in the workspace and are bounded.
+lik_status check_split(lik_dtype dtype, const Shapes& s) {
+  if (dtype != LIK_F32_BF16X3 || !lik::split_supported(s.layout, s.dim)) return LIK_OK;
+  const int64_t need = lik::split_bytes(s.q_rows, s.d_rows, s.dim);
+  if (need > lik::kSplitMaxBytes)
+    return fail(LIK_ERR_UNSUPPORTED,
+                "LIK_F32_BF16X3: the split copies of Q and D would take %lld bytes (at most %lld); "
+                "use LIK_F32",
+                (long long)need, (long long)lik::kSplitMaxBytes);
+  return LIK_OK;
+}
+
 bool is_zero_problem(const Shapes& s) { return s.pairs == 0; }
 
 lik_status forward_entry(int layout, const void* Q, const void* D, lik_dtype dtype, int64_t nq_or_b,
@@ -146,6 +158,7 @@ lik_status forward_entry(int layout, const void* Q, const void* D, lik_dtype dty
       !aligned16(workspace))
     return fail(LIK_ERR_INVALID_ARG, "Q, D, scores, argmax and workspace must be 16-byte aligned");
   st = check_supported(dtype, s);
+  if (st == LIK_OK) st = check_split(dtype, s);
   if (st != LIK_OK) return st;
   lik::FwdPlan p = lik::make_fwd_plan(layout, (int)dtype, nq_or_b, Lq, nd_or_n, Ld, dim,
                                       d_mask != nullptr, argmax != nullptr, q_mask != nullptr);
@@ -201,6 +214,7 @@ lik_status backward_entry(int layout, const void* Q, const void* D, lik_dtype dt
     return fail(LIK_ERR_INVALID_ARG,
                 "Q, D, argmax, gradients and workspace must be 16-byte aligned");
   st = check_supported(dtype, s);
+  if (st == LIK_OK && !argmax) st = check_split(dtype, s);   // the recomputing forward
   if (st != LIK_OK) return st;
   lik::BwdPlan p = lik::make_bwd_plan(layout, (int)dtype, nq_or_b, Lq, nd_or_n, Ld, dim,
                                       d_mask != nullptr, argmax != nullptr, q_mask != nullptr);
@@ -266,7 +280,10 @@ size_t lik_workspace_bytes(lik_op op, int64_t nq_or_b, int64_t lq, int64_t nd_or
     default: return SIZE_MAX;
   }
   Shapes s{layout, nq_or_b, lq, nd_or_n, ld, dim, 0, 0, 0, 0};
-  if (check_shapes(dtype == LIK_F32 || dtype == LIK_F16 || dtype == LIK_BF16 ? dtype : LIK_BF16,
+  if (check_shapes(dtype == LIK_F32 || dtype == LIK_F16 || dtype == LIK_BF16 ||
+                           dtype == LIK_F32_BF16X3
+                       ? dtype
+                       : LIK_BF16,
                    s) != LIK_OK)
     return SIZE_MAX;
   const bool has_dmask = (flags & 2) != 0;
@@ -287,7 +304,7 @@ int64_t fwd_plan_value(const lik::FwdPlan& p, const char* key) {
   const KV kv[] = {{"nb", p.NB},           {"upw", p.upw},         {"n_groups", p.n_groups},
                    {"n_sb", p.n_sb},       {"nchunks", p.nchunks}, {"tpc", p.tpc},
                    {"compact", p.compact}, {"partial", p.partial}, {"qpw", p.qpw},
-                   {"n_units", p.n_units}, {"n_cg", p.n_cg}};
+                   {"n_units", p.n_units}, {"n_cg", p.n_cg},       {"split", p.elem == 3}};
   for (const KV& e : kv)
     if (std::strcmp(key, e.k) == 0) return e.v;
   return -1;

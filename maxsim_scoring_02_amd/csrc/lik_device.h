@@ -29,12 +29,17 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kTile = 32;   // document rows per tile (MFMA M)
 constexpr int kWave = 64;
 
-enum class Elem { F16 = 0, BF16 = 1, F32 = 2 };
+// BF16S: float32 values held as two bfloat16 parts, a row of dim values
+// stored as 2 * dim bfloat16 [hi(0..dim) | lo(0..dim)] with hi = bf16(x) and
+// lo = bf16(x - hi); the kernels see a bfloat16 row of twice the width and
+// multiply it with three products per element pair (hi*hi, lo*hi, hi*lo).
+enum class Elem { F16 = 0, BF16 = 1, F32 = 2, BF16S = 3 };
 
 template <Elem E> struct ElemInfo;
 template <> struct ElemInfo<Elem::F16>  { static constexpr int kBytes = 2; static constexpr int kPerChunk = 8; };
 template <> struct ElemInfo<Elem::BF16> { static constexpr int kBytes = 2; static constexpr int kPerChunk = 8; };
 template <> struct ElemInfo<Elem::F32>  { static constexpr int kBytes = 4; static constexpr int kPerChunk = 4; };
+template <> struct ElemInfo<Elem::BF16S> { static constexpr int kBytes = 2; static constexpr int kPerChunk = 8; };
 
 // Geometry of one document row / tile for an element type and embedding dim.
 template <Elem E, int DIM>
@@ -71,6 +76,10 @@ __device__ __forceinline__ void st_lds_16(char* base, int off, u32x4 v) {
 template <Elem E> __device__ __forceinline__ void mfma_chunk(f32x16& acc, u32x4 a, u32x4 b);
 
 template <> __device__ __forceinline__ void mfma_chunk<Elem::BF16>(f32x16& acc, u32x4 a, u32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma_chunk<Elem::BF16S>(f32x16& acc, u32x4 a, u32x4 b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }

@@ -241,6 +241,19 @@ constexpr int ap_lds_bytes() {
 // acc = C + A * B over one tile, C the tile's initial value (zero with
 // ZERO, else c0: -inf in the rows a mask removes).  The first K-step reads C
 // and writes acc, so the initial value is never copied into the accumulators.
+// With split float32 rows (BF16S, K-steps 0..n-1 the high parts and n..2n-1
+// the low parts of both operands) the A chunk of a high K-step m meets the
+// query's high and low parts (B m and m + n) and that of a low K-step meets
+// the query's high part (B m - n): the three products hi*hi, hi*lo, lo*hi.
+template <Elem E, int KS>
+__device__ __forceinline__ constexpr int split_b(int m) {
+  return (E == Elem::BF16S && m >= KS / 2) ? m - KS / 2 : m;
+}
+template <Elem E, int KS>
+__device__ __forceinline__ constexpr bool split_second(int m) {
+  return E == Elem::BF16S && m < KS / 2;
+}
+
 template <Elem E, int DIM, int NB, bool ZERO>
 __device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
                                             const u32x4 (&bf)[NB][Geo<E, DIM>::kKSteps],
@@ -258,9 +271,15 @@ __device__ __forceinline__ void mfma_tile_c(f32x16 (&acc)[NB], const char* buf,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (m == 0) acc[b] = mfma_first<E, ZERO>(av[0], bf[b][0], c0);
-      else mfma_chunk<E>(acc[b], av[m], bf[b][m]);
+      else mfma_chunk<E>(acc[b], av[m], bf[b][split_b<E, KS>(m)]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk, 0);
+    if (split_second<E, KS>(m)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) mfma_chunk<E>(acc[b], av[m], bf[b][m + KS / 2]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerChunk, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk, 0);
+    }
     if (m + kWin < KS) {
       av[m + kWin] = ld_lds_16(buf, a_off + (m + kWin) * 32);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -291,19 +310,29 @@ __device__ __forceinline__ void mfma_pair_run(f32x16 (&xa)[NB], f32x16 (&xb)[NB]
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWin, 0);
 #pragma unroll
   for (int m = 0; m < KS; ++m) {
+    constexpr int kH = KS / 2;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (m == 0) xa[b] = mfma_first<E, ZERO>(aa[0], bf[b][0], ca);
-      else mfma_chunk<E>(xa[b], aa[m], bf[b][m]);
+      else mfma_chunk<E>(xa[b], aa[m], bf[b][split_b<E, KS>(m)]);
     }
     // without a second tile, its chains stop after the first K-step: every
     // row started at -inf (cb), so -inf is already their final value
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (m == 0) xb[b] = mfma_first<E, ZERO>(ab[0], bf[b][0], cb);
-      else if (twob) mfma_chunk<E>(xb[b], ab[m], bf[b][m]);
+      else if (twob) mfma_chunk<E>(xb[b], ab[m], bf[b][split_b<E, KS>(m)]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerChunk, 0);
+    if (split_second<E, KS>(m)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) mfma_chunk<E>(xa[b], aa[m], bf[b][m + kH]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (twob) mfma_chunk<E>(xb[b], ab[m], bf[b][m + kH]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kMfmaPerChunk, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaPerChunk, 0);
+    }
     if (m + kWin < KS) {
       aa[m + kWin] = ld_lds_16(bufa, a_off + (m + kWin) * 32);
       ab[m + kWin] = ld_lds_16(bufb, a_off + (m + kWin) * 32);
@@ -330,9 +359,6 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   constexpr int kSTRows = kSub * kTile;
   constexpr int kSTBytes = kSub * PD::kTileBytes;
   constexpr int kSTChunks = kSTRows * G::kCPR;
-  constexpr int kLoads = kSTChunks / kApThreads;
-  constexpr int kRowsPerLoad = kApThreads / G::kCPR;       // rows one load step covers
-  constexpr int kBytesPerLoad = kApThreads * 16;
   static_assert(kSTChunks % kApThreads == 0 && kApThreads % G::kCPR == 0,
                 "super-tile chunks must split evenly over the workgroup");
   constexpr uint32_t kFull = 0xffffffffu;
@@ -1067,7 +1093,7 @@ static hipError_t launch_fwd(K kernel, dim3 grid, dim3 block, size_t lds, hipStr
 template <Elem E, int DIM, int NB, bool MASK, bool KEEP>
 static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
   using G = Geo<E, DIM>;
-  if (p.layout == kAllPairs) {
+  if (E == Elem::BF16S || p.layout == kAllPairs) {
     const int64_t grid = 8 * p.gpx * p.n_sb;
     constexpr int lds = ap_lds_bytes<E, DIM>();
     if (lds > 65536) {
@@ -1079,10 +1105,13 @@ static hipError_t launch_main_m(const FwdPlan& p, const FwdArgs& a, hipStream_t 
     return launch_fwd(allpairs_fwd_kernel<E, DIM, NB, MASK, KEEP>, dim3((unsigned)grid),
                       dim3(kApThreads), lds, s, a);
   }
-  constexpr int W = pr_waves<E, DIM>();
-  const int64_t grid = cdiv(p.n_units, W);
-  return launch_fwd(pairs_fwd_kernel<E, DIM, NB, MASK>, dim3((unsigned)grid), dim3(W * kWave),
-                    W * G::kTileBytes, s, a);
+  if constexpr (E != Elem::BF16S) {   // split rows are only made for all-pairs
+    constexpr int W = pr_waves<E, DIM>();
+    const int64_t grid = cdiv(p.n_units, W);
+    return launch_fwd(pairs_fwd_kernel<E, DIM, NB, MASK>, dim3((unsigned)grid), dim3(W * kWave),
+                      W * G::kTileBytes, s, a);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <Elem E, int DIM, int NB>
@@ -1106,7 +1135,72 @@ static hipError_t dispatch_dim(const FwdPlan& p, const FwdArgs& a, hipStream_t s
   }
 }
 
+// Split float32 rows: the kernels see bfloat16 rows of 2 * dim.
+static hipError_t dispatch_split(const FwdPlan& p, const FwdArgs& a, hipStream_t s) {
+  switch (p.dim) {
+    case 64: return p.NB == 2 ? launch_main<Elem::BF16S, 128, 2>(p, a, s)
+                              : launch_main<Elem::BF16S, 128, 1>(p, a, s);
+    case 128: return launch_main<Elem::BF16S, 256, 1>(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 bool fwd_dim_supported(int64_t dim) { return dim == 64 || dim == 128 || dim == 256; }
+
+// bfloat16 bits of x rounded to nearest, ties to even (a NaN stays a NaN)
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Float32 rows of DIM values -> rows of 2 * DIM bfloat16 [hi | lo]:
+// hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in float32), so that
+// x = hi + lo + e with |e| <= 2^-16 |x|.  A value whose high part is not
+// finite gets lo = 0.  Thread = 8 consecutive values of a row.
+template <int DIM>
+__global__ __launch_bounds__(256) void split_f32_kernel(const float* __restrict__ x, int64_t rows,
+                                                        uint32_t* __restrict__ y) {
+  constexpr int kG = DIM / 8;   // groups of 8 per row
+  const int64_t n = rows * kG;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < n; g += (int64_t)gridDim.x * 256) {
+    const int64_t r = g / kG;
+    const int c = (int)(g - r * kG);
+    const float4 v0 = reinterpret_cast<const float4*>(x)[2 * g];
+    const float4 v1 = reinterpret_cast<const float4*>(x)[2 * g + 1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      hb[k] = bf16_bits_rne(v[k]);
+      const float h = __uint_as_float(hb[k] << 16);
+      lb[k] = __builtin_isfinite(h) ? bf16_bits_rne(v[k] - h) : 0u;
+    }
+    u32x4 ho, lo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ho[k] = hb[2 * k] | (hb[2 * k + 1] << 16);
+      lo[k] = lb[2 * k] | (lb[2 * k + 1] << 16);
+    }
+    // a split row is DIM 32-bit words: hi in words [0, DIM/2), lo after
+    uint32_t* row = y + r * DIM;
+    *reinterpret_cast<u32x4*>(row + c * 4) = ho;
+    *reinterpret_cast<u32x4*>(row + DIM / 2 + c * 4) = lo;
+  }
+}
+
+static hipError_t split_rows(const void* x, int64_t rows, int dim, char* out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t n = rows * (dim / 8);
+  const int64_t blocks = cdiv(n, 256) < 8192 ? cdiv(n, 256) : 8192;
+  if (dim == 64)
+    hipLaunchKernelGGL(split_f32_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const float*>(x), rows, reinterpret_cast<uint32_t*>(out));
+  else
+    hipLaunchKernelGGL(split_f32_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const float*>(x), rows, reinterpret_cast<uint32_t*>(out));
+  return hipGetLastError();
+}
 
 hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uint8_t* q_mask,
                        const uint8_t* d_mask, float* scores, int32_t* argmax, char* ws,
@@ -1172,9 +1266,17 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
     if (e0 != hipSuccess) return e0;
   }
   hipError_t e;
+  if (p.elem == 3) {   // float32 inputs scored through split bfloat16 rows
+    e = split_rows(Q, p.Nq * p.Lq, p.dim, ws + p.off_sq, s);
+    if (e == hipSuccess) e = split_rows(D, p.n_docs * p.Ld, p.dim, ws + p.off_sd, s);
+    if (e != hipSuccess) return e;
+    a.Q = ws + p.off_sq;
+    a.D = ws + p.off_sd;
+  }
   switch (p.elem) {
     case 0: e = dispatch_dim<Elem::F16>(p, a, s); break;
     case 1: e = dispatch_dim<Elem::BF16>(p, a, s); break;
+    case 3: e = dispatch_split(p, a, s); break;
     default: e = dispatch_dim<Elem::F32>(p, a, s); break;
   }
   if (e != hipSuccess) return e;

@@ -13,7 +13,7 @@ enum Layout : int { kAllPairs = 0, kPairwise = 1, kKd = 2 };
 
 struct FwdPlan {
   int layout = 0;
-  int elem = 0;             // 0 f16, 1 bf16, 2 f32
+  int elem = 0;             // 0 f16, 1 bf16, 2 f32, 3 f32 through split bf16 rows
   int dim = 0;
   int NB = 2;               // 32-column MFMA blocks per wave
   int SPW = 64;             // query-token slots per wave (32 * NB)
@@ -41,8 +41,20 @@ struct FwdPlan {
   int64_t n_units = 0;      // pairs: waves launched
   // workspace layout (bytes)
   size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, off_tok = 0, off_inv = 0,
-         off_cnt = 0, fwd_bytes = 0;
+         off_cnt = 0, off_sq = 0, off_sd = 0, fwd_bytes = 0;
 };
+
+// Split float32 rows (elem 3) are made for the all-pairs forward at these
+// dims; every other call with elem 3 computes exactly in float32 (elem 2).
+inline bool split_supported(int layout, int64_t dim) {
+  return layout == kAllPairs && (dim == 64 || dim == 128);
+}
+// the split copies of Q and D (as many bytes as the float32 inputs) stay
+// within this part of the workspace
+constexpr int64_t kSplitMaxBytes = int64_t(1) << 30;
+inline int64_t split_bytes(int64_t q_rows, int64_t d_rows, int64_t dim) {
+  return (q_rows + d_rows) * dim * 4;
+}
 
 // grad_D strategies
 enum GdMode : int {
@@ -115,10 +127,12 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
                              bool keep_argmax, bool has_qmask = false) {
   (void)keep_argmax;
   FwdPlan p;
+  if (elem == 3 && !split_supported(layout, dim)) elem = 2;
   p.layout = layout;
   p.elem = elem;
   p.dim = (int)dim;
-  p.NB = blocks_per_wave(elem, dim);
+  // split rows are bfloat16 rows of twice the width
+  p.NB = elem == 3 ? blocks_per_wave(1, 2 * dim) : blocks_per_wave(elem, dim);
   // a pair has one query: one 32-column block suffices when Lq <= 32
   if (layout != kAllPairs && Lq <= 32) p.NB = 1;
   p.SPW = 32 * p.NB;
@@ -224,6 +238,12 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
     p.off_partJ = off;
     off = align256(off + n * 4);
   }
+  if (p.elem == 3) {
+    p.off_sq = off;
+    off = align256(off + (size_t)p.Nq * Lq * dim * 4);
+    p.off_sd = off;
+    off = align256(off + (size_t)p.n_docs * Ld * dim * 4);
+  }
   p.fwd_bytes = off;
   return p;
 }
@@ -241,7 +261,7 @@ inline BwdPlan make_bwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq, 
   while (bits < 31 && (int64_t(1) << bits) < Ld) ++bits;
   b.key_bits = bits;
   // grad_D strategy
-  const int esize = elem == 2 ? 4 : 2;
+  const int esize = elem >= 2 ? 4 : 2;   // float32 inputs (exact or split)
   const int64_t q_bytes = f.Nq * Lq * dim * esize;
   if (layout == kAllPairs && b.H <= 65535 && Ld <= 65535 && Lq > 0 && Ld > 0 &&
       q_bytes < (int64_t(1) << 32)) {

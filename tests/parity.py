@@ -41,18 +41,18 @@ def to_gpu(w):
     return c(w.Q), c(w.D), c(w.q_mask), c(w.d_mask)
 
 
-def gpu_forward(w, keep_argmax=True):
+def gpu_forward(w, keep_argmax=True, fp32_split=False):
     Q, D, qm, dm = to_gpu(w)
-    s, a = _lib.FORWARD[w.layout](Q, D, qm, dm, keep_argmax=keep_argmax)
+    s, a = _lib.FORWARD[w.layout](Q, D, qm, dm, keep_argmax=keep_argmax, fp32_split=fp32_split)
     torch.cuda.synchronize()
     return s.cpu().numpy(), (None if a is None else a.cpu().numpy())
 
 
-def gpu_backward(w, grad, argmax=None):
+def gpu_backward(w, grad, argmax=None, fp32_split=False):
     Q, D, qm, dm = to_gpu(w)
     g = torch.as_tensor(grad, dtype=torch.float32).cuda().contiguous()
     am = None if argmax is None else torch.as_tensor(argmax, dtype=torch.int32).cuda().contiguous()
-    gQ, gD = _lib.BACKWARD[w.layout](Q, D, g, am, qm, dm)
+    gQ, gD = _lib.BACKWARD[w.layout](Q, D, g, am, qm, dm, fp32_split=fp32_split)
     torch.cuda.synchronize()
     return gQ.cpu().numpy(), gD.cpu().numpy()
 
@@ -91,13 +91,14 @@ def check_grads(gpu_g, ref_g, name):
     return rel
 
 
-def full_check(w, grad=None, keep_argmax=True, backward=True):
-    """Forward (+ backward) on the GPU against the oracle.  Returns a summary."""
+def full_check(w, grad=None, keep_argmax=True, backward=True, fp32_split=False):
+    """Forward (+ backward) on the GPU against the oracle.  Returns a summary.
+    fp32_split: float32 inputs through LIK_F32_BF16X3 (same tolerances)."""
     say(f"[parity] {w.name} layout={w.layout} dtype={w.dtype} Q={tuple(w.Q.shape)} "
-        f"D={tuple(w.D.shape)}")
+        f"D={tuple(w.D.shape)}{' fp32_split' if fp32_split else ''}")
     Qn, Dn, qm, dm = w.numpy_inputs()
     ref = ORACLE_FWD[w.layout](Qn, Dn, qm, dm)
-    s, a = gpu_forward(w, keep_argmax=keep_argmax)
+    s, a = gpu_forward(w, keep_argmax=keep_argmax, fp32_split=fp32_split)
     out = {"score_err": check_scores(s, ref)}
     merged = ref.argmax
     if keep_argmax:
@@ -105,7 +106,7 @@ def full_check(w, grad=None, keep_argmax=True, backward=True):
         out["ties"] = int(ref.tie.sum())
     if backward:
         g = w.grad.numpy() if grad is None else np.asarray(grad, dtype=np.float32)
-        gQ, gD = gpu_backward(w, g, a if keep_argmax else None)
+        gQ, gD = gpu_backward(w, g, a if keep_argmax else None, fp32_split=fp32_split)
         rQ, rD = ORACLE_BWD[w.layout](Qn, Dn, g.astype(np.float64), merged, qm, dm)
         out["gq_rel"] = check_grads(gQ, rQ, "grad_Q")
         out["gd_rel"] = check_grads(gD, rD, "grad_D")

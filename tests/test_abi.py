@@ -14,6 +14,19 @@ from maxsim_scoring_02_amd._lib import (LIK_BF16, LIK_ERR_INVALID_ARG, LIK_ERR_U
                                         LIK_OP_KD_BWD, LIK_OP_KD_FWD, LIK_OP_PAIRWISE_BWD,
                                         LIK_OP_PAIRWISE_FWD)
 
+def _no_gpu() -> bool:
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+# Calls that pass every host check go on to the device: with fake pointers
+# they are only made where no GPU is visible (they then stop at the device
+# check); with a GPU present those assertions are skipped.
+NO_GPU = _no_gpu()
+
 P = ctypes.c_void_p
 FAKE = P(0x1000)          # 16-byte aligned, never dereferenced
 MIS = P(0x1004)           # misaligned
@@ -121,12 +134,14 @@ def test_backward_rejects_invalid_arguments(L):
     # sort, which takes rows in windows and has no row limit: the call passes
     # every shape check and stops only at the device check here
     assert _lib.lik_plan_value(LIK_OP_BWD, (2, 32, 3, 40000, 128), LIK_BF16, 1, "gd_mode") == 0
-    assert bwd(L, Ld=40000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
-    assert "device" in L.lik_last_error().decode()
+    if NO_GPU:
+        assert bwd(L, Ld=40000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
+        assert "device" in L.lik_last_error().decode()
     # 20000 rows still fit the LDS sort
     assert _lib.lik_plan_value(LIK_OP_BWD, (2, 32, 3, 20000, 128), LIK_BF16, 1, "gd_mode") == 1
-    assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
-    assert "device" in L.lik_last_error().decode()
+    if NO_GPU:
+        assert bwd(L, Ld=20000, dm=None, wsb=1 << 40) == LIK_ERR_UNSUPPORTED
+        assert "device" in L.lik_last_error().decode()
 
 
 def test_long_pairwise_and_kd_backward_pass_the_shape_checks(L):
@@ -268,3 +283,42 @@ def test_noalloc_forward_limits_are_checked_on_the_host(L):
                                     None, None) == LIK_OK
     assert L.lik_maxsim_fwd_noalloc(FAKE, FAKE, LIK_BF16, 2, 32, 3, 40, 100, None, None, FAKE,
                                     None, None) == LIK_ERR_UNSUPPORTED
+
+
+def test_split_fp32_plan_workspace_and_limits(L):
+    """LIK_F32_BF16X3: the all-pairs forward at dim 64/128 scores through
+    split copies of Q and D held in the workspace (as many bytes as the
+    float32 inputs) on bfloat16 rows of twice the width; every other call
+    keeps the exact float32 plan; copies beyond 1 GiB are refused on the host."""
+    X3 = _lib.LIK_F32_BF16X3
+    dims = (256, 32, 256, 300, 128)
+    pv = lambda op, key, dt, d=dims, flags=3: _lib.lik_plan_value(op, d, dt, flags, key)
+    assert pv(LIK_OP_FWD, "split", X3) == 1 and pv(LIK_OP_FWD, "split", LIK_F32) == 0
+    # dim 128 split rows are 256 bfloat16 wide: one column block per wave, as bf16 at dim 256
+    assert pv(LIK_OP_FWD, "nb", X3) == 1
+    assert pv(LIK_OP_FWD, "nb", X3, (256, 32, 256, 300, 64)) == 2
+    extra = (256 * 32 + 256 * 300) * 128 * 4
+    w = lambda op, dt, d=dims, flags=3: L.lik_workspace_bytes(op, *d, dt, flags)
+    assert extra <= w(LIK_OP_FWD, X3) - w(LIK_OP_FWD, LIK_F32) <= extra + 512
+    # the backward holds the copies only when it recomputes the forward
+    assert w(LIK_OP_BWD, X3, flags=3) == w(LIK_OP_BWD, LIK_F32, flags=3)
+    assert w(LIK_OP_BWD, X3, flags=2) > w(LIK_OP_BWD, LIK_F32, flags=2)
+    assert pv(LIK_OP_BWD, "split", X3, flags=2) == 1
+    # pairwise, kd and dim 256 keep the exact float32 plans
+    for op, d in ((LIK_OP_PAIRWISE_FWD, (64, 32, 1, 2048, 128)),
+                  (LIK_OP_KD_FWD, (16, 32, 8, 1030, 128)),
+                  (LIK_OP_FWD, (64, 32, 64, 300, 256))):
+        assert pv(op, "split", X3, d) == 0
+        assert w(op, X3, d) == w(op, LIK_F32, d)
+    # copies above 1 GiB: UNSUPPORTED before any device work, naming LIK_F32
+    big = dict(dtype=X3, Nq=16, Lq=32, Nd=300, Ld=8192, dm=None, wsb=1 << 40)
+    assert (16 * 32 + 300 * 8192) * 128 * 4 > 1 << 30
+    assert fwd(L, **big) == LIK_ERR_UNSUPPORTED
+    assert "LIK_F32" in L.lik_last_error().decode()
+    assert bwd(L, argmax=None, **big) == LIK_ERR_UNSUPPORTED
+    # given the argmax, the backward makes no copies: shape checks pass and
+    # the call stops at the device check
+    if NO_GPU:
+        assert bwd(L, **big) == LIK_ERR_UNSUPPORTED
+        assert "device" in L.lik_last_error().decode()
+    assert fwd(L, dtype=4) == LIK_ERR_INVALID_ARG
