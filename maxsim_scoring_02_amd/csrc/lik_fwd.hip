@@ -1157,13 +1157,21 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
 // Float32 rows of DIM values -> rows of 2 * DIM bfloat16 [hi | lo]:
 // hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in float32), so that
 // x = hi + lo + e with |e| <= 2^-16 |x|.  A value whose high part is not
-// finite gets lo = 0.  Thread = 8 consecutive values of a row.
+// finite gets lo = 0.  Thread = 8 consecutive values of a row; one launch
+// splits Q (groups [0, nq)) and D (groups [nq, nq + nd)).
 template <int DIM>
-__global__ __launch_bounds__(256) void split_f32_kernel(const float* __restrict__ x, int64_t rows,
-                                                        uint32_t* __restrict__ y) {
+__global__ __launch_bounds__(256) void split_f32_kernel(const float* __restrict__ xq,
+                                                        uint32_t* __restrict__ yq, int64_t nq,
+                                                        const float* __restrict__ xd,
+                                                        uint32_t* __restrict__ yd, int64_t nd) {
   constexpr int kG = DIM / 8;   // groups of 8 per row
-  const int64_t n = rows * kG;
-  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < n; g += (int64_t)gridDim.x * 256) {
+  const int64_t n = nq + nd;
+  for (int64_t gg = (int64_t)blockIdx.x * 256 + threadIdx.x; gg < n;
+       gg += (int64_t)gridDim.x * 256) {
+    const bool isq = gg < nq;
+    const int64_t g = isq ? gg : gg - nq;
+    const float* x = isq ? xq : xd;
+    uint32_t* y = isq ? yq : yd;
     const int64_t r = g / kG;
     const int c = (int)(g - r * kG);
     const float4 v0 = reinterpret_cast<const float4*>(x)[2 * g];
@@ -1189,16 +1197,22 @@ __global__ __launch_bounds__(256) void split_f32_kernel(const float* __restrict_
   }
 }
 
-static hipError_t split_rows(const void* x, int64_t rows, int dim, char* out, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  const int64_t n = rows * (dim / 8);
-  const int64_t blocks = cdiv(n, 256) < 8192 ? cdiv(n, 256) : 8192;
+// Q (q_rows rows) and D (d_rows rows) into their split copies, one launch.
+static hipError_t split_rows(const void* Q, int64_t q_rows, char* q_out, const void* D,
+                             int64_t d_rows, char* d_out, int dim, hipStream_t s) {
+  const int64_t nq = q_rows * (dim / 8), nd = d_rows * (dim / 8);
+  if (nq + nd == 0) return hipSuccess;
+  const int64_t blocks = cdiv(nq + nd, 256) < 8192 ? cdiv(nq + nd, 256) : 8192;
+  const float* xq = static_cast<const float*>(Q);
+  const float* xd = static_cast<const float*>(D);
+  uint32_t* yq = reinterpret_cast<uint32_t*>(q_out);
+  uint32_t* yd = reinterpret_cast<uint32_t*>(d_out);
   if (dim == 64)
-    hipLaunchKernelGGL(split_f32_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const float*>(x), rows, reinterpret_cast<uint32_t*>(out));
+    hipLaunchKernelGGL(split_f32_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, xq, yq, nq,
+                       xd, yd, nd);
   else
-    hipLaunchKernelGGL(split_f32_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const float*>(x), rows, reinterpret_cast<uint32_t*>(out));
+    hipLaunchKernelGGL(split_f32_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, xq, yq, nq,
+                       xd, yd, nd);
   return hipGetLastError();
 }
 
@@ -1267,8 +1281,7 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
   }
   hipError_t e;
   if (p.elem == 3) {   // float32 inputs scored through split bfloat16 rows
-    e = split_rows(Q, p.Nq * p.Lq, p.dim, ws + p.off_sq, s);
-    if (e == hipSuccess) e = split_rows(D, p.n_docs * p.Ld, p.dim, ws + p.off_sd, s);
+    e = split_rows(Q, p.Nq * p.Lq, ws + p.off_sq, D, p.n_docs * p.Ld, ws + p.off_sd, p.dim, s);
     if (e != hipSuccess) return e;
     a.Q = ws + p.off_sq;
     a.D = ws + p.off_sd;
