@@ -166,3 +166,22 @@ def test_inbatch_text_f32_split_full_size():
     assert _lib.lik_plan_value(_lib.LIK_OP_FWD, dims, X3, 3, "upw") > 1
     out = full_check(w, fp32_split=True)
     say(f"[fullsize] inbatch-text-f32x3: {out}")
+
+
+def test_split_through_the_allocation_free_forward():
+    """lik_maxsim_fwd_noalloc with LIK_F32_BF16X3 keeps the split copies in
+    its fixed scratch: bitwise equal to the workspace forward, twice in a
+    row with a smaller call between."""
+    rng = np.random.default_rng(2400)
+    dev = torch.device("cuda:0")
+    cases = []
+    for Nq, Nd, Ld in ((12, 40, 300), (5, 7, 70)):
+        Q = torch.from_numpy(_tokens(rng, (Nq, 32, 128))).to(dev)
+        D = torch.from_numpy(_tokens(rng, (Nd, Ld, 128))).to(dev)
+        dm = torch.from_numpy(np.arange(Ld)[None] < rng.integers(1, Ld + 1, Nd)[:, None]).to(dev)
+        cases.append((Q, D, dm))
+    for Q, D, dm in (cases[0], cases[1], cases[0]):
+        s0, a0 = _lib.lik_maxsim_fwd(Q, D, None, dm, fp32_split=True)
+        s1, a1 = _lib.lik_maxsim_fwd_noalloc(Q, D, None, dm, fp32_split=True)
+        torch.cuda.synchronize()
+        assert torch.equal(s0, s1) and torch.equal(a0, a1)

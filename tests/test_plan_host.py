@@ -98,8 +98,27 @@ static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     CHECK(p.n_units == p.n_docs * p.n_cg * p.nchunks, "pairs units");
   }
   const size_t offs[] = {p.off_bits, p.off_tiles, p.off_partM, p.off_partJ, p.off_tok, p.off_inv,
-                         p.off_cnt};
+                         p.off_cnt, p.off_sq, p.off_sd};
   for (size_t o : offs) CHECK(o % 256 == 0 && o <= p.fwd_bytes, "fwd offset %zu / %zu", o, p.fwd_bytes);
+  // float32 through split rows: only all-pairs at dim 64 / 128, bf16 rows of
+  // twice the width (NB of bf16 at 2 * dim), the copies after every other
+  // region and inside the workspace
+  if (elem == 3) {
+    const bool split = layout == kAllPairs && (dim == 64 || dim == 128);
+    CHECK(p.elem == (split ? 3 : 2), "split elem %d", p.elem);
+    if (split) {
+      CHECK(p.NB == blocks_per_wave(1, 2 * dim), "split NB %d", p.NB);
+      size_t other_end = 0;
+      if (mask) other_end = p.off_tiles + (size_t)p.n_docs * 4;
+      if (p.compact) other_end = p.off_cnt + 4;
+      if (p.partial)
+        other_end = p.off_partJ + (size_t)p.nchunks * p.n_docs * p.n_cg * p.SPW * 4;
+      CHECK(p.off_sq >= other_end, "split copies after the other regions");
+      CHECK(p.off_sd >= p.off_sq + (size_t)p.Nq * Lq * dim * 4 &&
+                p.off_sd + (size_t)p.n_docs * Ld * dim * 4 <= p.fwd_bytes,
+            "split copies inside the workspace");
+    }
+  }
 }
 
 static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, long dim) {
@@ -110,7 +129,7 @@ static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     // every LDS region inside the allocation and disjoint from the others,
     // the keys and histograms (sorting) and the partial rows (summing) in the
     // same region, and Q rows addressed with 32-bit offsets
-    const long esize = elem == 2 ? 4 : 2;
+    const long esize = elem >= 2 ? 4 : 2;
     const long cpr = dim * esize / 16;
     const size_t part = (size_t)(kGsThreads / cpr) * 2 * dim * 4;
     CHECK(layout == kAllPairs, "sorted grad_D only for all-pairs");
@@ -147,7 +166,7 @@ static void bwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
           "sort regions");
   }
   if (b.gq_ap) {
-    const long esize = elem == 2 ? 4 : 2;
+    const long esize = elem >= 2 ? 4 : 2;
     CHECK(layout == kAllPairs && b.gq_slices >= 1, "grad_Q rounds");
     CHECK(((b.fwd.n_docs + b.gq_slices - 1) / b.gq_slices) * Ld * dim * esize < (1L << 32),
           "slice offsets");
@@ -173,7 +192,7 @@ int main() {
   const long Lds[] = {1, 31, 32, 33, 300, 1030, 2049, 2111, 8192, 32768};
   const long Nqs[] = {1, 2, 16, 128, 256};
   const long Nds[] = {1, 4, 75, 256, 1000};
-  for (int elem = 0; elem < 3; ++elem)
+  for (int elem = 0; elem < 4; ++elem)
     for (long dim : dims)
       for (long Lq : Lqs)
         for (long Ld : Lds)
@@ -189,7 +208,7 @@ int main() {
             }
   // hit lists past the sorted kernel's 16-bit hit numbers: the workspace sort
   // in one batch, several batches, and one document per batch
-  for (int elem = 0; elem < 3; ++elem) {
+  for (int elem = 0; elem < 4; ++elem) {
     bwd_case(kAllPairs, elem, 2100, 32, 150, 64, 128);
     bwd_case(kAllPairs, elem, 2100, 32, 600, 64, 128);
     bwd_case(kAllPairs, elem, 20000, 32, 1000, 300, 128);
