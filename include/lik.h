@@ -68,7 +68,8 @@
 extern "C" {
 #endif
 
-#define LIK_ABI_VERSION 1
+/* 2: adds LIK_F32_BF16X3 (version 1 callers are unaffected). */
+#define LIK_ABI_VERSION 2
 
 /*
  * Input element types.  LIK_F16, LIK_BF16 and LIK_F32 are the input types of

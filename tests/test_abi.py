@@ -52,7 +52,7 @@ def test_profile_events_need_both_or_neither(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.lik_abi_version() == 1
+    assert L.lik_abi_version() == 2
     assert L.lik_status_string(LIK_OK) == b"ok"
     assert L.lik_status_string(LIK_ERR_INVALID_ARG) == b"invalid argument"
     assert L.lik_status_string(LIK_ERR_UNSUPPORTED) == b"unsupported"
