@@ -26,8 +26,10 @@
 //                          16 hits per round prepared one per lane; rows cut by
 //                          a share boundary are finished by the group where
 //                          they start
-//     gradd_pairs_kernel   pairwise / kd: four waves per document stream its
-//                          (mostly zero) rows and sum the few hit rows inline
+//     gradd_pairs_kernel   pairwise / kd: waves per document stream its rows
+//                          as zeros, then store the few rows with hits again
+//                          with their sums (grads_pairs_kernel runs it beside
+//                          the grad_Q gather in one launch)
 //     gradd_sort_*_kernel + gradd_rows_group_kernel
 //                          general fallback through the workspace
 #include <hip/hip_runtime.h>
@@ -956,6 +958,7 @@ __device__ __forceinline__ void gradd_pairs_body(const BwdArgs& a, int64_t block
   constexpr int RPI = F4 >= 64 ? 1 : 64 / F4; // rows per wave store
   constexpr int NH = kPairsMaxLq / 64;        // hit registers per lane
   constexpr int ES = ElemInfo<E>::kBytes;
+  constexpr int kNone = 0x7fffffff;
   static_assert(F4 <= 64, "one gradient row per wave store at most");
   const int lane = threadIdx.x & 63;
   // gd_parts waves per document, each streaming a contiguous share of its
@@ -970,61 +973,60 @@ __device__ __forceinline__ void gradd_pairs_body(const BwdArgs& a, int64_t block
   const int r_begin = (int)((int64_t)n_st * part / parts) * RPI;
   const int r_end = min((int)((int64_t)n_st * (part + 1) / parts) * RPI, Ld);
   const int nh = (Lq + 63) / 64;
-  const float g = a.g[e];
-  const int64_t qbase = (e / a.K) * a.Lq;     // first Q row of this document's query
+  // the hits' rows are requested first; the zero stream below does not
+  // wait for them
   int key[NH];
 #pragma unroll
   for (int k = 0; k < NH; ++k) {
     const int h = 64 * k + lane;
-    int j = -1;
-    if (k < nh && h < Lq) j = a.argmax[e * a.Lq + h];
-    key[k] = (j >= 0 && j < Ld) ? j : -1;
+    key[k] = (k < nh && h < Lq) ? a.argmax[e * a.Lq + h] : -1;
   }
+  const float g = a.g[e];
   const int sub = lane / F4, f = lane - (lane / F4) * F4;
   float* out = a.gD + e * (int64_t)Ld * DIM;
+  // 1. every row of the share as zeros; a row with hits is stored again
+  // below, by the same lanes, so its sum lands after its zeros
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int r0 = r_begin; r0 < r_end; r0 += RPI) {
+    const int row = r0 + sub;
+    if (sub < RPI && row < r_end) *reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f) = z;
+  }
+  // 2. the rows of the share that have hits, in increasing row order, each
+  // the sum of g * Q[h] over its hits in increasing h
+#pragma unroll
+  for (int k = 0; k < NH; ++k) key[k] = (key[k] >= r_begin && key[k] < r_end) ? key[k] : kNone;
   const char* Qb = (const char*)a.Q;
-  // U stores (U * RPI rows) per hit check, so several stores are in flight
-  // and the check is paid once for them; each row is still written once,
-  // with its hits added in increasing h
-  constexpr int U = 4;
-  for (int r0 = r_begin; r0 < r_end; r0 += RPI * U) {
-    bool any = false;
+  const int64_t qbase = (e / a.K) * a.Lq;     // first Q row of this document's query
+  while (true) {
+    int m = key[0];
 #pragma unroll
-    for (int k = 0; k < NH; ++k) any |= (k < nh) && key[k] >= r0 && key[k] < r0 + RPI * U;
-    float v[U][4];
+    for (int k = 1; k < NH; ++k) m = min(m, key[k]);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int o = 32; o >= 1; o >>= 1) m = min(m, __shfl_xor(m, o));
+    const int row = __builtin_amdgcn_readfirstlane(m);
+    if (row == kNone) break;
+    const bool mine = sub == (row - r_begin) % RPI;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v[u][t] = 0.f;
-    if (__ballot(any) != 0ull) {
+    for (int k = 0; k < NH; ++k) {
+      if (k >= nh) break;
+      uint64_t mk = __ballot(key[k] == row);
+      while (mk != 0ull) {
+        const int b = __ffsll((unsigned long long)mk) - 1;
+        mk &= mk - 1;
+        if (mine) {
+          float x[4];
+          load4_as_float<E>(Qb + (qbase + 64 * k + b) * (int64_t)(DIM * ES) + 4 * f * ES, x);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        for (int rr = 0; rr < RPI; ++rr) {
-#pragma unroll
-          for (int k = 0; k < NH; ++k) {
-            if (k >= nh) break;
-            uint64_t m = __ballot(key[k] == r0 + u * RPI + rr);
-            while (m != 0ull) {
-              const int b = __ffsll((unsigned long long)m) - 1;
-              m &= m - 1;
-              if (sub == rr) {
-                float x[4];
-                load4_as_float<E>(Qb + (qbase + 64 * k + b) * (int64_t)(DIM * ES) + 4 * f * ES, x);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[u][t] = __builtin_fmaf(g, x[t], v[u][t]);
-              }
-            }
-          }
+          for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(g, x[t], v[t]);
         }
       }
+      key[k] = key[k] == row ? kNone : key[k];
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = r0 + u * RPI + sub;
-      if (sub < RPI && row < r_end) {
-        const f32x4 w = {v[u][0], v[u][1], v[u][2], v[u][3]};
-        *reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f) = w;
-      }
+    if (mine) {
+      const f32x4 w = {v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(out + (int64_t)row * DIM + 4 * f) = w;
     }
   }
 }
