@@ -185,3 +185,28 @@ def test_split_through_the_allocation_free_forward():
         s1, a1 = _lib.lik_maxsim_fwd_noalloc(Q, D, None, dm, fp32_split=True)
         torch.cuda.synchronize()
         assert torch.equal(s0, s1) and torch.equal(a0, a1)
+
+
+def test_split_degenerate_shapes_equal_exact_float32():
+    """Shapes where the split has nothing to multiply follow the same rules
+    as LIK_F32, bitwise: queries with no tokens (Lq = 0), every document
+    empty, fully masked queries, single documents and single queries."""
+    rng = np.random.default_rng(2500)
+    cases = [
+        _w("x3-lq0", "allpairs", np.zeros((3, 0, 128), np.float32), _tokens(rng, (4, 50, 128))),
+        _w("x3-all-empty", "allpairs", _tokens(rng, (3, 32, 128)), _tokens(rng, (4, 50, 128)),
+           dm=np.zeros((4, 50), bool)),
+        _w("x3-masked-queries", "allpairs", _tokens(rng, (3, 32, 64)), _tokens(rng, (4, 70, 64)),
+           qm=np.array([[False] * 32, [True] * 32, [False] * 31 + [True]])),
+        _w("x3-one-doc", "allpairs", _tokens(rng, (5, 33, 128)), _tokens(rng, (1, 97, 128))),
+        _w("x3-one-query", "allpairs", _tokens(rng, (1, 7, 64)), _tokens(rng, (9, 31, 64))),
+    ]
+    for w in cases:
+        s0, a0 = gpu_forward(w)
+        s1, a1 = gpu_forward(w, fp32_split=True)
+        ref = ORACLE_FWD["allpairs"](*w.numpy_inputs())
+        check_scores(s1, ref)
+        empty = ref.scores == oracle.EMPTY_DOC_SCORE
+        assert np.array_equal(s0[empty], s1[empty]), w.name
+        if w.Q.shape[1] == 0 or not (~empty).any():
+            assert np.array_equal(s0, s1) and np.array_equal(a0, a1), w.name
