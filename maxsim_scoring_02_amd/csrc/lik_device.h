@@ -165,15 +165,15 @@ __device__ __forceinline__ void tile_init(f32x16& c, uint32_t word, int h) {
 template <int V>
 __device__ __forceinline__ float tile_init_elem(uint32_t word, float ninf, float zero) {
   constexpr int b0 = 8 * (V >> 2) + (V & 3);
+  // lane mask = (bit b0 of word ? all of lanes 0-31) | (bit b0+4 ? all of
+  // 32-63): two sign-extended 1-bit fields, one per half of the mask.  Each
+  // element's mask is its own register pair, so the selects do not wait on
+  // the next element's mask overwriting a shared condition register.
+  const uint32_t lo = (uint32_t)(-(int32_t)((word >> b0) & 1u));
+  const uint32_t hi = (uint32_t)(-(int32_t)((word >> (b0 + 4)) & 1u));
+  const uint64_t mask = (uint64_t)lo | ((uint64_t)hi << 32);
   float r;
-  // vcc = (bit b0 of word ? all of lanes 0-31) | (bit b0+4 ? all of 32-63):
-  // two sign-extended 1-bit fields, one per half of vcc
-  asm("s_bfe_i32 vcc_lo, %1, %4\n\t"
-      "s_bfe_i32 vcc_hi, %1, %5\n\t"
-      "v_cndmask_b32_e32 %0, %2, %3, vcc"
-      : "=v"(r)
-      : "s"(word), "v"(ninf), "v"(zero), "i"(b0 | (1 << 16)), "i"((b0 + 4) | (1 << 16))
-      : "vcc");
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(ninf), "v"(zero), "s"(mask));
   return r;
 }
 __device__ __forceinline__ void tile_init_uniform(f32x16& c, uint32_t word) {
@@ -334,10 +334,30 @@ __device__ __forceinline__ void state_update(BlockState& s, f32x16 acc, uint32_t
 }
 
 // (max, lowest doc row reaching it) of this lane's half-column.
+// (mask bit of this lane ? V : a), V an inline constant
+template <int V>
+__device__ __forceinline__ int sel_mask_const(int a, uint64_t mask) {
+  int r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "n"(V), "s"(mask));
+  return r;
+}
+template <int V>
+__device__ __forceinline__ int lowest_equal(const uint64_t (&eq)[15], int kk) {
+  if constexpr (V < 0) {
+    return kk;
+  } else {
+    return lowest_equal<V - 1>(eq, sel_mask_const<V>(kk, eq[V]));
+  }
+}
+
 __device__ __forceinline__ void state_resolve(const BlockState& s, int h, float& M, int& J) {
-  int kk = 15;
+  // every compare writes its own lane mask first, then the selects read
+  // them: compares chained through one condition register would each wait
+  // two cycles before their select
+  uint64_t eq[15];
 #pragma unroll
-  for (int v = 14; v >= 0; --v) kk = (s.best_val[v] == s.run_max) ? v : kk;
+  for (int v = 0; v < 15; ++v) eq[v] = __builtin_amdgcn_ballot_w64(s.best_val[v] == s.run_max);
+  const int kk = lowest_equal<14>(eq, 15);
   M = s.run_max;
   J = s.best_tile * kTile + acc_row(kk, h);
 }
