@@ -27,7 +27,9 @@ constexpr float kEmptyDocScore = -1e9f;
 
 // ---------------------------------------------------------------------------
 // mask prep: one workgroup of 4 waves per document; every load is issued
-// before any is used, and the last valid word is the maximum over the waves.
+// before any is used, blocks past the document's end form no words (a short
+// document's waves skip most of their unrolled pass: long documents
+// 7.2 -> 5.9 us), and the last valid word is the maximum over the waves.
 // - byte path: a wave reads 64 consecutive mask bytes (one per lane) and a
 //   ballot of "byte != 0" is directly two tile words;
 // - dword path (mask rows 4-byte aligned): a lane reads 4 bytes, forms their
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(256) void mask_prep_kernel(const uint8_t* __restric
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        if (b0 + (int64_t)u * NWV >= nblk) break;   // uniform: past the document
         uint32_t nib = ((v[u] & 0xffu) != 0) | (((v[u] >> 8) & 0xffu) != 0) << 1 |
                        (((v[u] >> 16) & 0xffu) != 0) << 2 | ((v[u] >> 24) != 0) << 3;
         uint32_t word = nib << (4 * (lane & 7));
@@ -78,6 +81,7 @@ __global__ __launch_bounds__(256) void mask_prep_kernel(const uint8_t* __restric
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        if (b0 + (int64_t)u * NWV >= nblk) break;   // uniform: past the document
         const uint64_t bal = __ballot(v[u] != 0);
         const int64_t w = 2 * (b0 + (int64_t)u * NWV);
         if (lane < 2 && w + lane < nwords) out[w + lane] = (uint32_t)(bal >> (32 * lane));
@@ -117,7 +121,6 @@ __global__ void fill_scores_no_query_tokens_kernel(float* scores, int64_t n_out,
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void compact_prep_kernel(const uint8_t* __restrict__ q_mask,
                                                             int64_t n, int32_t* __restrict__ tok,
-                                                            int32_t* __restrict__ inv,
                                                             int32_t* __restrict__ cnt) {
   constexpr int T = 1024, PER = 16, NWV = T / 64;
   __shared__ int wsum[NWV];
@@ -151,16 +154,7 @@ __global__ __launch_bounds__(1024) void compact_prep_kernel(const uint8_t* __res
     int slot = carry + wbase + incl - c;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int64_t j = t0 + k;
-      if (j < n) {
-        if (m[k]) {
-          tok[slot] = (int32_t)j;
-          inv[j] = slot;
-          ++slot;
-        } else {
-          inv[j] = -1;
-        }
-      }
+      if (t0 + k < n && m[k]) tok[slot++] = (int32_t)(t0 + k);
     }
     carry += total;
     __syncthreads();                       // wsum is rewritten by the next block
@@ -612,7 +606,6 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
   // queries of 32 tokens two to a wave: their sums are lane-aligned halves
   const bool fast_sum = a.qpw > 0 && a.Lq == 32;
   const int64_t score_base = slot_q * a.n_docs;
-  const int64_t part_lane = (int64_t)gw * SPW + L;
   if (second) {
     if (my_loads == kMyLoads) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMyLoads));
@@ -745,8 +738,8 @@ __global__ __launch_bounds__(kApThreads) void allpairs_fwd_kernel(FwdArgs a) {
       int Jv;
       combine_halves<NB>(M, J, lane, Mv, Jv);
       if (a.partial) {
-        if (writer) {
-          const int64_t idx = ((int64_t)cc * a.n_docs + cd) * a.n_cg * SPW + part_lane;
+        if (writer && slot_ok) {
+          const int64_t idx = ((int64_t)cc * a.n_docs + cd) * a.n_cg * SPW + slot_q * a.Lq + slot_i;
           a.part_M[idx] = has ? Mv : -__builtin_inff();
           if constexpr (KEEP) a.part_J[idx] = has ? Jv : -1;
         }
@@ -904,6 +897,26 @@ __global__ __launch_bounds__(256) void pairs_fwd_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // combine: one wave per output (query, doc) / pair
 // ---------------------------------------------------------------------------
+// Offset of token i's chunk-0 partials for output (q, document or pair e),
+// and whether the token has partials.  The all-pairs kernel writes them in
+// token order (document e, then q * Lq + i), only for tokens with a slot:
+// with compacted tokens the masked ones have none, and their (never
+// written) entries are read and then dropped, so the mask load and the
+// partial loads issue together.  The pairwise / kd kernel writes them by
+// (pair e, slot group, slot).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t partial_base(const FwdArgs& a, bool ap, int64_t q, int64_t e,
+                                                int64_t i, bool ok, bool& have) {
+  if (ap) {
+    have = ok && (!a.compact || a.q_mask[q * a.Lq + i] != 0);
+    return e * a.n_cg * a.SPW + q * a.Lq + i;
+  }
+  have = ok;
+  const int64_t cg = i / a.SPW;
+  return (e * a.n_cg + cg) * a.SPW + (i - cg * a.SPW);
+}
+
+// ---------------------------------------------------------------------------
 // Many chunks: one workgroup per output.  Its 256 threads are TG query-token
 // lanes (32, or 64 when Lq > 32) x G = 256 / TG chunk groups; a thread merges
 // the chunks c = g, g + G, ... with all of its loads issued before any is
@@ -929,30 +942,11 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
     for (int64_t i0 = 0; i0 < a.Lq; i0 += TG) {
       const int64_t i = i0 + tl;
       const bool ok = i < a.Lq;
-      int64_t cg, slot;
-      bool have = ok;                        // this token has partials
-      if (ap && a.compact) {
-        const int32_t s2 = ok ? a.tok_inv[q * a.Lq + i] : -1;
-        have = s2 >= 0;
-        cg = have ? s2 / a.SPW : 0;
-        slot = have ? s2 - cg * a.SPW : 0;
-      } else if (ap) {
-        if (a.qpw > 0) {
-          cg = q / a.qpw;
-          slot = (q - cg * a.qpw) * a.Lq + i;
-        } else {
-          const int64_t s = q * a.Lq + i;
-          cg = s / a.SPW;
-          slot = s - cg * a.SPW;
-        }
-      } else {
-        cg = i / a.SPW;
-        slot = i - cg * a.SPW;
-      }
+      bool have;                             // this token has partials
+      const int64_t base = partial_base(a, ap, q, e, i, ok, have);
       float M = -__builtin_inff();
       int J = -1;
-      if (have) {
-        const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
+      if (ok) {
         constexpr int U = 16;
         for (int64_t c0 = grp; c0 < a.nchunks; c0 += (int64_t)G * U) {
           float mm[U];
@@ -970,6 +964,10 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(FwdArgs a) {
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) merge_mj(M, J, mm[u], jj[u]);
+        }
+        if (!have) {
+          M = -__builtin_inff();
+          J = -1;
         }
       }
       sM[grp][tl] = M;
@@ -1017,30 +1015,11 @@ __global__ __launch_bounds__(256) void combine_fwd_wave_kernel(FwdArgs a) {
     for (int64_t i0 = 0; i0 < a.Lq; i0 += gs) {
       const int64_t i = i0 + li;
       const bool ok = i < a.Lq;
-      int64_t cg, slot;
-      bool have = ok;                        // this token has partials
-      if (ap && a.compact) {
-        const int32_t s2 = ok ? a.tok_inv[q * a.Lq + i] : -1;
-        have = s2 >= 0;
-        cg = have ? s2 / a.SPW : 0;
-        slot = have ? s2 - cg * a.SPW : 0;
-      } else if (ap) {
-        if (a.qpw > 0) {
-          cg = q / a.qpw;
-          slot = (q - cg * a.qpw) * a.Lq + i;
-        } else {
-          const int64_t s2 = q * a.Lq + i;
-          cg = s2 / a.SPW;
-          slot = s2 - cg * a.SPW;
-        }
-      } else {
-        cg = i / a.SPW;
-        slot = i - cg * a.SPW;
-      }
+      bool have;                             // this token has partials
+      const int64_t base = partial_base(a, ap, q, e, i, ok, have);
       float M = -__builtin_inff();
       int J = -1;
-      if (have) {
-        const int64_t base = (e * a.n_cg + cg) * a.SPW + slot;
+      if (ok) {
         constexpr int U = 4;
         for (int64_t c0 = 0; c0 < a.nchunks; c0 += U) {
           float mm[U];
@@ -1057,6 +1036,10 @@ __global__ __launch_bounds__(256) void combine_fwd_wave_kernel(FwdArgs a) {
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) merge_mj(M, J, mm[u], jj[u]);
+        }
+        if (!have) {
+          M = -__builtin_inff();
+          J = -1;
         }
       }
       const bool tok = ok && (!a.q_mask || a.q_mask[q * a.Lq + i]);
@@ -1272,10 +1255,9 @@ hipError_t run_forward(const FwdPlan& p, const void* Q, const void* D, const uin
   if (p.compact) {
     a.compact = 1;
     a.tok = reinterpret_cast<int32_t*>(ws + p.off_tok);
-    a.tok_inv = reinterpret_cast<int32_t*>(ws + p.off_inv);
     a.tok_cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
     hipLaunchKernelGGL(compact_prep_kernel, dim3(1), dim3(1024), 0, s, q_mask, p.Nq * p.Lq, a.tok,
-                       a.tok_inv, a.tok_cnt);
+                       a.tok_cnt);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }

@@ -17,12 +17,13 @@ struct FwdArgs {
   int32_t* ntiles;    // [n_docs] tiles up to the last valid token, or null
   float* scores;
   int32_t* argmax;
-  float* part_M;            // partial maxima  [nchunks][n_docs][n_cg][SPW]
+  // partial maxima [nchunks][n_docs][n_cg * SPW]: all-pairs by token
+  // (q * Lq + i, tokens with a slot only), pairwise / kd by (slot group, slot)
+  float* part_M;
   int32_t* part_J;          // partial argmaxes, same layout
   // compacted query tokens (all-pairs with a query mask): slot s holds token
-  // tok[s] = q * Lq + i for s < *tok_cnt; tok_inv[q * Lq + i] is its slot or -1
+  // tok[s] = q * Lq + i for s < *tok_cnt
   int32_t* tok;
-  int32_t* tok_inv;
   int32_t* tok_cnt;
   int compact;
   int layout;

@@ -40,7 +40,7 @@ struct FwdPlan {
   int64_t n_groups = 0, gpx = 0;
   int64_t n_units = 0;      // pairs: waves launched
   // workspace layout (bytes)
-  size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, off_tok = 0, off_inv = 0,
+  size_t off_bits = 0, off_tiles = 0, off_partM = 0, off_partJ = 0, off_tok = 0,
          off_cnt = 0, off_sq = 0, off_sd = 0, fwd_bytes = 0;
 };
 
@@ -228,8 +228,6 @@ inline FwdPlan make_fwd_plan(int layout, int elem, int64_t nq_or_b, int64_t Lq,
   if (p.compact) {
     const size_t nt = (size_t)p.Nq * Lq;
     p.off_tok = off;
-    off = align256(off + nt * 4);
-    p.off_inv = off;
     off = align256(off + nt * 4);
     p.off_cnt = off;
     off = align256(off + 4);

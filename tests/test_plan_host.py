@@ -57,8 +57,8 @@ static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     CHECK(layout == kAllPairs && qmask, "compact only for all-pairs with a query mask");
     CHECK(p.partial && p.qpw == 0, "compact uses the split path");
     CHECK(p.n_cg * p.SPW >= p.Nq * Lq, "compact slots cover every token");
-    CHECK(p.off_tok % 256 == 0 && p.off_inv >= p.off_tok + (size_t)p.Nq * Lq * 4 &&
-              p.off_cnt >= p.off_inv + (size_t)p.Nq * Lq * 4 && p.off_cnt + 4 <= p.fwd_bytes,
+    CHECK(p.off_tok % 256 == 0 && p.off_cnt >= p.off_tok + (size_t)p.Nq * Lq * 4 &&
+              p.off_cnt + 4 <= p.fwd_bytes,
           "compact tables");
   } else if (layout == kAllPairs && qmask && Lq > 1) {
     CHECK(p.Nq * Lq > kCompactMaxTokens, "a query mask compacts unless the token list is too long");
@@ -97,7 +97,7 @@ static void fwd_case(int layout, int elem, long Nq, long Lq, long Nd, long Ld, l
     CHECK(p.nchunks * p.tpc >= p.ntiles_max, "pairs chunks");
     CHECK(p.n_units == p.n_docs * p.n_cg * p.nchunks, "pairs units");
   }
-  const size_t offs[] = {p.off_bits, p.off_tiles, p.off_partM, p.off_partJ, p.off_tok, p.off_inv,
+  const size_t offs[] = {p.off_bits, p.off_tiles, p.off_partM, p.off_partJ, p.off_tok,
                          p.off_cnt, p.off_sq, p.off_sd};
   for (size_t o : offs) CHECK(o % 256 == 0 && o <= p.fwd_bytes, "fwd offset %zu / %zu", o, p.fwd_bytes);
   // float32 through split rows: only all-pairs at dim 64 / 128, bf16 rows of
