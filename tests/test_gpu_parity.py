@@ -222,6 +222,26 @@ def test_doc_lengths_and_tails(Ld):
     full_check(_custom(f"ld{Ld}-pair", "pairwise", "f16", Q, D[:3], None, None, g[:, 0]))
 
 
+@pytest.mark.parametrize("Lq,Ld", [(20, 2100), (100, 300)])
+def test_partials_without_a_query_mask(Lq, Ld):
+    """Per-token partials of uncompacted slots: three queries of 20 tokens
+    per wave (4 slots unused) with documents cut into chunks, and queries of
+    100 tokens spanning waves; only slots that hold a token write partials,
+    and the combine reads each token's at its (q, i) position."""
+    from maxsim_scoring_02_amd import _lib
+    rng = np.random.default_rng(700 + Lq)
+    Nq, Nd, dim = 5, 4, 128
+    dims = (Nq, Lq, Nd, Ld, dim)
+    pv = lambda key: _lib.lik_plan_value(_lib.LIK_OP_FWD, dims, _lib.LIK_BF16, 1 | 2, key)
+    assert pv("partial") == 1 and pv("compact") == 0
+    assert (pv("qpw"), pv("nchunks") > 1) == ((3, True) if Lq == 20 else (0, False))
+    Q = _rand_tokens(rng, (Nq, Lq, dim))
+    D = _rand_tokens(rng, (Nd, Ld, dim))
+    dm = np.arange(Ld)[None] < rng.integers(1, Ld + 1, Nd)[:, None]
+    g = rng.standard_normal((Nq, Nd))
+    full_check(_custom(f"partials-lq{Lq}-ld{Ld}", "allpairs", "bf16", Q, D, None, dm, g))
+
+
 def test_many_documents_grad_q_per_xcd_slice():
     """Nd >= 64: grad_Q is gathered per document slice (one slice per XCD)
     and the slice partials are added in order."""
